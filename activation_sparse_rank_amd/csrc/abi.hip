@@ -1,0 +1,257 @@
+// The C ABI of libpi (declared in include/pi.h): host-side validation,
+// workspace layout and the launch sequence of each entry point.  Every
+// argument check happens before the first launch, so a rejected call has no
+// effect on the device.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "pi.h"
+#include "pi_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pi_status hip_fail(hipError_t e) {
+  g_last_error = hipGetErrorString(e);
+  return PI_E_HIP;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int elems_per_chunk(int wtype) { return wtype == PI_F16 ? 8 : (wtype == PI_F32 ? 4 : 32); }
+
+pi_status check_pred(const pi_predictor* p) {
+  if (!p) return PI_E_NULL;
+  if (p->wtype != PI_F16 && p->wtype != PI_F32) return PI_E_DTYPE;
+  if (p->d_model <= 0 || p->rank <= 0 || p->d_ff <= 0) return PI_E_SHAPE;
+  if (p->rank % 8 || p->rank > 4096) return PI_E_SHAPE;
+  if (p->d_model % elems_per_chunk(p->wtype)) return PI_E_SHAPE;
+  if (!p->p1 || !p->p2 || !p->c) return PI_E_NULL;
+  if (!al16(p->p1) || !al16(p->p2) || !al16(p->c)) return PI_E_ALIGN;
+  return PI_OK;
+}
+
+pi_status check_ffn(const pi_ffn* f) {
+  if (!f) return PI_E_NULL;
+  if (f->wtype != PI_F16 && f->wtype != PI_F32 && f->wtype != PI_Q4_0) return PI_E_DTYPE;
+  if (f->act != PI_RELU && f->act != PI_REGLU && f->act != PI_RELU2) return PI_E_DTYPE;
+  if (f->d_model <= 0 || f->d_ff <= 0) return PI_E_SHAPE;
+  if (f->d_model % elems_per_chunk(f->wtype)) return PI_E_SHAPE;
+  if (!f->w_up || !f->w_down_t) return PI_E_NULL;
+  if (f->act == PI_REGLU && !f->w_gate) return PI_E_NULL;
+  if (!al16(f->w_up) || !al16(f->w_down_t)) return PI_E_ALIGN;
+  if (f->act == PI_REGLU && !al16(f->w_gate)) return PI_E_ALIGN;
+  if (f->b_up && !al16(f->b_up)) return PI_E_ALIGN;
+  if (f->b_gate && !al16(f->b_gate)) return PI_E_ALIGN;
+  if (f->wtype == PI_Q4_0) return PI_E_DTYPE;   // Q4_0 compute kernels not available yet
+  return PI_OK;
+}
+
+int x_type_of(const pi_ffn* f) { return f->wtype == PI_Q4_0 ? PI_F16 : f->wtype; }
+
+// Workspace: each entry point lays out only the sections it uses, in this
+// order, every section 256-byte aligned.
+struct Layout {
+  size_t t = 0, mask = 0, idx = 0, count = 0, h = 0, part = 0, total = 0;
+  int n_chunks = 0;
+};
+
+Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up256(bytes);
+    return o;
+  };
+  if (pred) L.t = take((size_t)n_tok * pred->rank * sizeof(float));
+  if (pred && ffn) {
+    L.mask = take((size_t)n_tok * ffn->d_ff);
+    L.idx = take((size_t)ffn->d_ff * sizeof(int32_t));
+    L.count = take(sizeof(int32_t));
+  }
+  if (ffn) {
+    const int tile = pi::sparse_tile(ffn->wtype, ffn->d_model);
+    const int nt = n_tok < tile ? n_tok : tile;
+    L.n_chunks = pi::sparse_chunks(ffn->wtype, ffn->d_model, ffn->d_ff, n_tok);
+    L.h = take((size_t)nt * ffn->d_ff * sizeof(float));
+    L.part = take((size_t)L.n_chunks * nt * ffn->d_model * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+pi_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return PI_E_WORKSPACE;
+  if (!al16(ws)) return PI_E_ALIGN;
+  if (ws_bytes < need) return PI_E_WORKSPACE;
+  return PI_OK;
+}
+
+pi_status check_tau(float tau) {
+  if (!(tau > 0.0f && tau < 1.0f)) return PI_E_RANGE;   // also rejects NaN
+  return PI_OK;
+}
+
+float theta_of(float tau) {
+  const double t = (double)tau;
+  return (float)log(t / (1.0 - t));
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+pi::SparseArgs sparse_args(const pi_ffn* f, const void* x, int n_tok, const int32_t* idx, const int32_t* count,
+                           int max_count, void* y, int ytype, char* ws, const Layout& L) {
+  pi::SparseArgs a;
+  a.wtype = f->wtype;
+  a.act = f->act;
+  a.d = f->d_model;
+  a.d_ff = f->d_ff;
+  a.n_tok = n_tok;
+  a.max_count = max_count;
+  a.w_up = f->w_up;
+  a.w_gate = f->act == PI_REGLU ? f->w_gate : nullptr;
+  a.w_down_t = f->w_down_t;
+  a.b_up = f->b_up;
+  a.b_gate = f->b_gate;
+  a.x = x;
+  a.idx = idx;
+  a.count = count;
+  a.y = y;
+  a.ytype = ytype;
+  a.h = reinterpret_cast<float*>(ws + L.h);
+  a.part = reinterpret_cast<float*>(ws + L.part);
+  a.n_chunks = L.n_chunks;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n_tok) {
+  if (n_tok < 1) return 0;
+  if (pred && check_pred(pred) != PI_OK) return 0;
+  if (ffn && check_ffn(ffn) != PI_OK) return 0;
+  if (!pred && !ffn) return 0;
+  return layout(pred, ffn, n_tok).total;
+}
+
+pi_status pi_predict(const pi_predictor* pred, const void* x, int32_t xtype, int32_t n_tok, float tau,
+                     uint8_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  pi_status st = check_pred(pred);
+  if (st != PI_OK) return st;
+  if (!x || !mask) return PI_E_NULL;
+  if (n_tok < 1) return PI_E_SHAPE;
+  if (xtype != pred->wtype) return PI_E_DTYPE;
+  if (!al16(x) || !al16(mask) || (logits && !al16(logits))) return PI_E_ALIGN;
+  if ((st = check_tau(tau)) != PI_OK) return st;
+  const Layout L = layout(pred, nullptr, n_tok);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != PI_OK) return st;
+  float* t = reinterpret_cast<float*>(static_cast<char*>(ws) + L.t);
+  hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t,
+                                           as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  e = pi::launch_predict_stage2(pred->wtype, pred->p2, pred->c, t, n_tok, pred->rank, pred->d_ff, theta_of(tau),
+                                mask, logits, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_compact(const uint8_t* mask, int32_t n_tok, int32_t d_ff, int32_t* idx, int32_t* count,
+                     void* stream) {
+  if (!mask || !idx || !count) return PI_E_NULL;
+  if (n_tok < 1 || d_ff < 1) return PI_E_SHAPE;
+  if (!al16(mask) || !al16(idx) || (reinterpret_cast<uintptr_t>(count) & 3u)) return PI_E_ALIGN;
+  const hipError_t e = pi::launch_compact(mask, n_tok, d_ff, idx, count, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_sparse_ffn(const pi_ffn* ffn, const void* x, int32_t xtype, int32_t n_tok, const int32_t* idx,
+                        const int32_t* count, int32_t max_count, void* y, int32_t ytype, void* ws,
+                        size_t ws_bytes, void* stream) {
+  pi_status st = check_ffn(ffn);
+  if (st != PI_OK) return st;
+  if (!x || !idx || !count || !y) return PI_E_NULL;
+  if (n_tok < 1) return PI_E_SHAPE;
+  if (xtype != x_type_of(ffn)) return PI_E_DTYPE;
+  if (ytype != PI_F32 && ytype != PI_F16) return PI_E_DTYPE;
+  if (max_count < 0 || max_count > ffn->d_ff) return PI_E_RANGE;
+  if (!al16(x) || !al16(idx) || !al16(y) || (reinterpret_cast<uintptr_t>(count) & 3u)) return PI_E_ALIGN;
+  const Layout L = layout(nullptr, ffn, n_tok);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != PI_OK) return st;
+  const pi::SparseArgs a =
+      sparse_args(ffn, x, n_tok, idx, count, max_count, y, ytype, static_cast<char*>(ws), L);
+  const hipError_t e = pi::launch_sparse_ffn(a, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int32_t xtype, int32_t n_tok,
+                   float tau, void* y, int32_t ytype, void* ws, size_t ws_bytes, void* stream) {
+  pi_status st = check_pred(pred);
+  if (st != PI_OK) return st;
+  if ((st = check_ffn(ffn)) != PI_OK) return st;
+  if (pred->d_model != ffn->d_model || pred->d_ff != ffn->d_ff) return PI_E_SHAPE;
+  if (!x || !y) return PI_E_NULL;
+  if (n_tok < 1) return PI_E_SHAPE;
+  if (xtype != pred->wtype || xtype != x_type_of(ffn)) return PI_E_DTYPE;
+  if (ytype != PI_F32 && ytype != PI_F16) return PI_E_DTYPE;
+  if (!al16(x) || !al16(y)) return PI_E_ALIGN;
+  if ((st = check_tau(tau)) != PI_OK) return st;
+  const Layout L = layout(pred, ffn, n_tok);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != PI_OK) return st;
+
+  char* w = static_cast<char*>(ws);
+  float* t = reinterpret_cast<float*>(w + L.t);
+  uint8_t* mask = reinterpret_cast<uint8_t*>(w + L.mask);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + L.idx);
+  int32_t* count = reinterpret_cast<int32_t*>(w + L.count);
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = pi::launch_predict_stage2(pred->wtype, pred->p2, pred->c, t, n_tok, pred->rank, pred->d_ff, theta_of(tau),
+                                mask, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = pi::launch_compact(mask, n_tok, ffn->d_ff, idx, count, s);
+  if (e != hipSuccess) return hip_fail(e);
+  const pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
+  e = pi::launch_sparse_ffn(a, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_q4_0_repack(const void* src, int32_t rows, int32_t cols, void* dst, void* stream) {
+  if (!src || !dst) return PI_E_NULL;
+  if (rows < 1 || cols < 32 || cols % 32) return PI_E_SHAPE;
+  const size_t bytes = (size_t)rows * (cols / 32) * 18;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return PI_E_RANGE;   // overlapping buffers
+  if (!al16(dst)) return PI_E_ALIGN;
+  const hipError_t e = pi::launch_q4_0_repack(src, rows, cols, dst, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+const char* pi_status_str(pi_status s) {
+  switch (s) {
+    case PI_OK: return "ok";
+    case PI_E_NULL: return "a required pointer is NULL";
+    case PI_E_SHAPE: return "a size is out of range or sizes disagree";
+    case PI_E_DTYPE: return "unsupported dtype or dtype/activation combination";
+    case PI_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case PI_E_RANGE: return "a value is out of range (tau, max_count, overlap)";
+    case PI_E_WORKSPACE: return "workspace missing or too small";
+    case PI_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pi_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

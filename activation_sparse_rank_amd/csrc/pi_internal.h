@@ -1,0 +1,122 @@
+// Internal declarations shared by the libpi sources: device helpers for
+// gfx950 (wave64) and the host-side launchers each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pi {
+
+// ---------------------------------------------------------------------------
+// Types
+// ---------------------------------------------------------------------------
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld_nt(const void* p) {
+  // Streaming weight rows: non-temporal so they do not evict reused data.
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ f16x2 as_h2(unsigned int v) { return __builtin_bit_cast(f16x2, v); }
+
+__device__ __forceinline__ float as_f(unsigned int v) { return __builtin_bit_cast(float, v); }
+
+// 8 fp16 products accumulated in fp32 (v_dot2_f32_f16: exact fp16 products,
+// fp32 accumulation).
+__device__ __forceinline__ float dot8_f16(u32x4 w, u32x4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2(as_h2(w.x), as_h2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(w.y), as_h2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(w.z), as_h2(x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(w.w), as_h2(x.w), acc, false);
+  return acc;
+}
+
+// 4 fp32 products accumulated in fp32.
+__device__ __forceinline__ float dot4_f32(u32x4 w, u32x4 x, float acc) {
+  acc = __builtin_fmaf(as_f(w.x), as_f(x.x), acc);
+  acc = __builtin_fmaf(as_f(w.y), as_f(x.y), acc);
+  acc = __builtin_fmaf(as_f(w.z), as_f(x.z), acc);
+  acc = __builtin_fmaf(as_f(w.w), as_f(x.w), acc);
+  return acc;
+}
+
+// Butterfly sum over the 64 lanes of a wave; every lane ends with the same
+// bits (each step adds the same two values in either order).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Butterfly sum over aligned groups of G lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Activation codes (match pi_act).
+enum : int { ACT_RELU = 0, ACT_REGLU = 1, ACT_RELU2 = 2 };
+
+// ---------------------------------------------------------------------------
+// Host launchers (each returns the hipError_t of its launch)
+// ---------------------------------------------------------------------------
+
+// t[n][r] = p1[r] . x[n]           (fp32 out)
+hipError_t launch_predict_stage1(int wtype, const void* p1, const void* x, int n_tok, int d,
+                                 int rank, float* t, hipStream_t s);
+// l[n][i] = p2[i] . t[n] + c[i];  mask[n][i] = l > theta
+hipError_t launch_predict_stage2(int wtype, const void* p2, const float* c, const float* t,
+                                 int n_tok, int rank, int d_ff, float theta, uint8_t* mask,
+                                 float* logits, hipStream_t s);
+// ascending list of neurons marked by any token
+hipError_t launch_compact(const uint8_t* mask, int n_tok, int d_ff, int32_t* idx, int32_t* count,
+                          hipStream_t s);
+
+// Sparse FFN (one call = all launches for n_tok tokens).
+struct SparseArgs {
+  int wtype, act, d, d_ff, n_tok, max_count;
+  const void* w_up;
+  const void* w_gate;
+  const void* w_down_t;
+  const float* b_up;
+  const float* b_gate;
+  const void* x;
+  const int32_t* idx;
+  const int32_t* count;
+  void* y;
+  int ytype;
+  float* h;        // workspace [n_tok][d_ff] fp32
+  float* part;     // workspace [n_chunks][n_tok][d] fp32
+  int n_chunks;
+};
+hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
+
+// Partial-sum chunk count and tokens per pass used for a given shape (they
+// size the workspace).
+int sparse_chunks(int wtype, int d, int d_ff, int n_tok);
+int sparse_tile(int wtype, int d);
+
+hipError_t launch_q4_0_repack(const void* src, int rows, int cols, void* dst, hipStream_t s);
+
+}  // namespace pi

@@ -1,0 +1,176 @@
+/*
+ * pi.h -- C ABI of libpi: a predictor-gated, neuron-aware sparse FFN for one
+ * AMD MI355X (gfx950).
+ *
+ * The method (PowerInfer, as three web pages describe it):
+ *  - [QB] QbitAI article on r-manual.ru, "2080 Ti может запускать большие
+ *    модели 70B ...", sections "Что такое «разреженная активация»?",
+ *    "Гибридный дизайн вывода CPU/GPU" (worked example: the predictor names
+ *    neurons 3, 4 and 5; each is computed where its weights live; the partial
+ *    results are merged) and "Общая архитектура PowerInfer".
+ *  - [GN] GeekNews, vi.news.hada.io topic 12458, sections "Cách suy luận lai
+ *    CPU/GPU" (adaptive predictor, neuron-aware sparse operators) and "Lượng
+ *    tử hóa và tương thích" (INT4 Q4_0).
+ *  - [AB] aibars.net profile "SJTU-IPADS/PowerInfer", sections "Componentes
+ *    Principais" and "Aprofundamento nos Princípios Técnicos".
+ *
+ * One decode layer: a small per-layer predictor guesses which FFN neurons an
+ * input activates (pi_predict), the guess becomes an ordered neuron list
+ * (pi_compact), and only those neurons' weight rows are read and computed
+ * (pi_sparse_ffn); pi_layer runs the three in sequence.  Every neuron stays
+ * resident in device memory: there is no host/device split of neurons.
+ *
+ * Conventions for every entry point:
+ *  - Ownership: every array pointer is DEVICE memory owned by the caller.  The
+ *    library allocates and frees nothing; scratch space comes from the
+ *    caller's workspace `ws` (see pi_workspace_bytes).  Descriptor structs
+ *    are host memory, read during the call only.  The library keeps no
+ *    mutable global state.
+ *  - Streams: calls are asynchronous and ordered on `stream` (a hipStream_t;
+ *    NULL = the default stream).  No call synchronises the host or copies
+ *    device->host, so every call may be captured into a HIP graph.
+ *  - Errors: arguments are validated on the host BEFORE anything is
+ *    launched; on any error the call returns a status and launches nothing.
+ *    A failed launch returns PI_E_HIP (pi_last_error() gives the HIP message,
+ *    per host thread).  Faults inside kernels surface at the caller's next
+ *    synchronisation of the stream.  No C++ exception crosses this ABI.
+ *  - Layout: matrices are row-major with one row per neuron.  Activations are
+ *    [n_tok][d_model].  All array pointers must be 16-byte aligned.
+ *  - Determinism: identical inputs give bitwise identical outputs on every
+ *    run (no atomics in any reduction; every sum has a fixed order).
+ */
+#ifndef PI_H_
+#define PI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pi_status {
+  PI_OK = 0,
+  PI_E_NULL = 1,      /* a required pointer is NULL */
+  PI_E_SHAPE = 2,     /* a size is out of range or sizes disagree */
+  PI_E_DTYPE = 3,     /* unsupported dtype, or dtype/activation combination */
+  PI_E_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  PI_E_RANGE = 5,     /* tau outside (0, 1), or max_count outside [0, d_ff] */
+  PI_E_WORKSPACE = 6, /* ws is NULL or smaller than required */
+  PI_E_HIP = 7        /* the HIP runtime refused a launch */
+} pi_status;
+
+typedef enum pi_dtype {
+  PI_F32 = 0,
+  PI_F16 = 1,
+  PI_Q4_0 = 2 /* 4-bit weights, 32 per block with one fp16 scale; see pi_q4_0_repack */
+} pi_dtype;
+
+typedef enum pi_act {
+  PI_RELU = 0,  /* h = max(w_up.x + b_up, 0)                       */
+  PI_REGLU = 1, /* h = max(w_gate.x + b_gate, 0) * (w_up.x)        */
+  PI_RELU2 = 2  /* h = max(w_up.x + b_up, 0)^2  (squared ReLU)     */
+} pi_act;
+
+/* Low-rank activation predictor of one layer ([QB] "Что такое «разреженная
+ * активация»?": a small model per layer, trained offline, predicts the
+ * neurons an input will activate).  Reading used: t = p1 x; logit
+ * l_i = p2_i . t + c_i; neuron i predicted active iff sigmoid(l_i) > tau.  */
+typedef struct pi_predictor {
+  int32_t d_model;   /* input width d                                   */
+  int32_t rank;      /* r; must be a multiple of 8                       */
+  int32_t d_ff;      /* number of neurons                                */
+  int32_t wtype;     /* PI_F16 or PI_F32                                 */
+  const void* p1;    /* [rank][d_model]                                  */
+  const void* p2;    /* [d_ff][rank]                                     */
+  const float* c;    /* [d_ff] logit bias                                */
+} pi_predictor;
+
+/* FFN weights of one layer.  Row i of w_down_t holds the weights neuron i
+ * adds into every output (the transposed down projection).  */
+typedef struct pi_ffn {
+  int32_t d_model;        /* multiple of 8 (F16), 4 (F32), 32 (Q4_0)      */
+  int32_t d_ff;
+  int32_t act;            /* pi_act                                        */
+  int32_t wtype;          /* PI_F32, PI_F16, or PI_Q4_0 (repacked layout)  */
+  const void* w_up;       /* [d_ff][d_model]                               */
+  const void* w_gate;     /* [d_ff][d_model] for PI_REGLU, else ignored    */
+  const void* w_down_t;   /* [d_ff][d_model]                               */
+  const float* b_up;      /* [d_ff] for RELU / RELU2; NULL = no bias       */
+  const float* b_gate;    /* [d_ff] for REGLU; NULL = no bias              */
+} pi_ffn;
+
+/* Bytes of workspace any call with these descriptors and n_tok tokens needs
+ * (the most any entry point asks for; pi_layer needs all of it).  Either
+ * descriptor may be NULL when the calls that need it are not made.  Returns
+ * 0 for invalid descriptors.  */
+size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n_tok);
+
+/* Predict which neurons each token activates.
+ *   x:      [n_tok][d_model], dtype xtype == pred->wtype
+ *   tau:    probability threshold in (0, 1); compared as l_i > ln(tau/(1-tau))
+ *           in fp32 (a NaN logit is inactive)
+ *   mask:   out [n_tok][d_ff] uint8, 1 = predicted active, 0 = not
+ *   logits: optional out [n_tok][d_ff] fp32 (may be NULL)
+ *   ws:     workspace (the first rank*n_tok*4 bytes are used)
+ * Cited passage: [QB] "Гибридный дизайн вывода CPU/GPU" (the prediction step
+ * of the worked example) and [GN] "Cách suy luận lai CPU/GPU".  */
+pi_status pi_predict(const pi_predictor* pred, const void* x, int32_t xtype, int32_t n_tok,
+                     float tau, uint8_t* mask, float* logits,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Turn masks into the ascending list of marked neurons.
+ *   mask:  [n_tok][d_ff] uint8; an entry marks its neuron when nonzero; with
+ *          n_tok > 1 the list is the union over tokens
+ *   idx:   out [d_ff] int32; entries [0, *count) are written, ascending
+ *   count: out, ONE int32 in device memory (never copied to the host)
+ * Cited passage: [QB] "Гибридный дизайн вывода CPU/GPU" (the predicted set
+ * {3, 4, 5}).  */
+pi_status pi_compact(const uint8_t* mask, int32_t n_tok, int32_t d_ff,
+                     int32_t* idx, int32_t* count, void* stream);
+
+/* FFN over listed neurons only; unlisted neurons contribute exactly zero.
+ *   x:         [n_tok][d_model]; xtype == ffn->wtype, or PI_F16 for Q4_0
+ *   idx:       device int32 list, strictly increasing, values in [0, d_ff)
+ *              (as pi_compact writes it); duplicates are undefined
+ *   count:     device int32: number of valid entries of idx
+ *   max_count: host bound on *count, in [0, d_ff]; sizes the launch (pass
+ *              d_ff when unknown).  A device count above max_count is clamped
+ *              to max_count.
+ *   y:         out [n_tok][d_model], ytype PI_F32 or PI_F16 (round to nearest
+ *              even); every token evaluates every listed neuron
+ * Cited passage: [QB] "Что такое «разреженная активация»?" (only the
+ * activated neurons are computed) and "Общая архитектура PowerInfer" (partial
+ * results merged into the output).  */
+pi_status pi_sparse_ffn(const pi_ffn* ffn, const void* x, int32_t xtype, int32_t n_tok,
+                        const int32_t* idx, const int32_t* count, int32_t max_count,
+                        void* y, int32_t ytype, void* ws, size_t ws_bytes, void* stream);
+
+/* One layer: pi_predict, pi_compact, pi_sparse_ffn on the same x.  The
+ * predictor and FFN must agree on d_model and d_ff.  Mask, list and count
+ * live in ws.  Cited passage: [QB] "Общая архитектура PowerInfer".  */
+pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int32_t xtype,
+                   int32_t n_tok, float tau, void* y, int32_t ytype,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Convert canonical Q4_0 blocks into the layout the kernels read.
+ *   src: [rows][cols/32] blocks of 18 bytes (little-endian fp16 scale d, then
+ *        16 bytes; byte j holds code j in its low nibble and code j+16 in its
+ *        high nibble; code q means weight d*(q-8))
+ *   dst: rows*cols/32*18 bytes: all rows' 16-byte code groups first
+ *        ([rows][cols/32][16]), then all scales ([rows][cols/32] fp16)
+ * cols must be a multiple of 32.  src and dst must not overlap.
+ * Cited passage: [GN] "Lượng tử hóa và tương thích" (INT4 Q4_0).  */
+pi_status pi_q4_0_repack(const void* src, int32_t rows, int32_t cols, void* dst, void* stream);
+
+/* Static text for a status code.  */
+const char* pi_status_str(pi_status s);
+
+/* Text of the last PI_E_HIP error on this host thread ("" if none).  */
+const char* pi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PI_H_ */
