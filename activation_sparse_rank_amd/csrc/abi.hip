@@ -56,8 +56,9 @@ int x_type_of(const pi_ffn* f) { return f->wtype == PI_Q4_0 ? PI_F16 : f->wtype;
 // Workspace: each entry point lays out only the sections it uses, in this
 // order, every section 256-byte aligned.
 struct Layout {
-  size_t t = 0, mask = 0, idx = 0, count = 0, h = 0, part = 0, total = 0;
-  int n_chunks = 0;
+  size_t t = 0, mask = 0, idx = 0, count = 0, status = 0, h = 0, part = 0;
+  size_t total = 0;
+  int n_chunks = 0, n_slices = 0, n_segments = 0;
 };
 
 Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
@@ -73,11 +74,12 @@ Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
     L.mask = take((size_t)n_tok * ffn->d_ff);
     L.idx = take((size_t)ffn->d_ff * sizeof(int32_t));
     L.count = take(sizeof(int32_t));
+    L.n_segments = pi::layer_segments(ffn->d_ff);
+    L.status = take((size_t)L.n_segments * sizeof(unsigned));
   }
   if (ffn) {
-    const int tile = pi::sparse_tile(ffn->wtype, ffn->d_model);
-    const int nt = n_tok < tile ? n_tok : tile;
-    L.n_chunks = pi::sparse_chunks(ffn->wtype, ffn->d_model, ffn->d_ff, n_tok);
+    const int nt = n_tok < pi::kSparseTile ? n_tok : pi::kSparseTile;
+    pi::sparse_chunking(ffn->wtype, ffn->d_model, &L.n_chunks, &L.n_slices);
     L.h = take((size_t)nt * ffn->d_ff * sizeof(float));
     L.part = take((size_t)L.n_chunks * nt * ffn->d_model * sizeof(float));
   }
@@ -126,6 +128,7 @@ pi::SparseArgs sparse_args(const pi_ffn* f, const void* x, int n_tok, const int3
   a.h = reinterpret_cast<float*>(ws + L.h);
   a.part = reinterpret_cast<float*>(ws + L.part);
   a.n_chunks = L.n_chunks;
+  a.n_slices = L.n_slices;
   return a;
 }
 
@@ -154,7 +157,7 @@ pi_status pi_predict(const pi_predictor* pred, const void* x, int32_t xtype, int
   if ((st = check_ws(ws, ws_bytes, L.total)) != PI_OK) return st;
   float* t = reinterpret_cast<float*>(static_cast<char*>(ws) + L.t);
   hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t,
-                                           as_stream(stream));
+                                           nullptr, 0, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e);
   e = pi::launch_predict_stage2(pred->wtype, pred->p2, pred->c, t, n_tok, pred->rank, pred->d_ff, theta_of(tau),
                                 mask, logits, as_stream(stream));
@@ -212,15 +215,34 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
   uint8_t* mask = reinterpret_cast<uint8_t*>(w + L.mask);
   int32_t* idx = reinterpret_cast<int32_t*>(w + L.idx);
   int32_t* count = reinterpret_cast<int32_t*>(w + L.count);
+  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   const hipStream_t s = as_stream(stream);
-  hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, s);
+  pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
+  const bool fused = n_tok <= pi::kSparseTile && n_tok <= pi::pred_tile(pred->rank);
+  // Stage 1 also clears the fused kernel's segment counters.
+  hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t,
+                                           fused ? status : nullptr, fused ? L.n_segments : 0, s);
   if (e != hipSuccess) return hip_fail(e);
+  if (fused) {
+    pi::LayerArgs la;
+    la.p2 = pred->p2;
+    la.c = pred->c;
+    la.t = t;
+    la.rank = pred->rank;
+    la.theta = theta_of(tau);
+    la.status = status;
+    la.idx = idx;
+    la.count = count;
+    e = pi::launch_layer_fused(a, la, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return PI_OK;
+  }
+  // Many tokens: predict every token, take the union list, then the list path.
   e = pi::launch_predict_stage2(pred->wtype, pred->p2, pred->c, t, n_tok, pred->rank, pred->d_ff, theta_of(tau),
                                 mask, nullptr, s);
   if (e != hipSuccess) return hip_fail(e);
   e = pi::launch_compact(mask, n_tok, ffn->d_ff, idx, count, s);
   if (e != hipSuccess) return hip_fail(e);
-  const pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
   e = pi::launch_sparse_ffn(a, s);
   if (e != hipSuccess) return hip_fail(e);
   return PI_OK;

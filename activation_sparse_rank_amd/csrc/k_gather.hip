@@ -1,25 +1,28 @@
-// Neuron-aware sparse FFN over a list of active neurons (fp16 / fp32 weights).
+// Neuron-aware sparse FFN over the active neurons (fp16 / fp32 weights).
 //
 // [QB] "Что такое «разреженная активация»?": only the activated neurons are
 // computed; the others add nothing.  [QB] "Гибридный дизайн вывода CPU/GPU"
 // and "Общая архитектура PowerInfer": the partial results of separately
 // computed neuron groups are merged into the layer output.  Here the groups
-// are chunks of the active list on one GPU and the merge is a fixed-order sum.
+// are chunks of the active-neuron list on one GPU and the merge is a
+// fixed-order sum.
 //
-// Three kernels per token tile:
-//   up    -- one wave per listed neuron: its w_up (and w_gate) row is read
-//            with 16-byte loads (1 KB per wave instruction), dotted with x,
-//            summed across the wave and passed through the activation;
-//            h[k] is written in fp32.
-//   down  -- a workgroup per (column slice, chunk of the list): each wave
-//            walks rows of the chunk and accumulates h[k] * w_down_t[idx[k]]
-//            over its slice (one 16-byte load per lane per row); the 8 waves
-//            are summed in LDS in wave order and the chunk's partial sums
-//            are written to the workspace.
-//   merge -- y = sum over chunks of the partials, in chunk order.
-// No atomics anywhere, and every sum has a fixed order, so y is bitwise
-// reproducible.  All three are bound by HBM bandwidth on the weight rows.
-#include "pi_internal.h"
+// Kernels:
+//   k_up       -- list path: one wave per listed neuron; its w_up (and w_gate)
+//                 row is read with 16-byte loads (1 KB per wave instruction),
+//                 dotted with x, summed across the wave and activated; h is
+//                 stored by neuron number.
+//   k_pred_up  -- layer path: the second predictor product, the up
+//                 projection and the compaction fused (see below).
+//   k_down     -- a workgroup per (column slice, chunk of the list): each wave
+//                 accumulates h_i * w_down_t[i] over its slice for the rows
+//                 of the chunk, the 8 waves are summed in LDS in wave order,
+//                 and the chunk's partial sums go to the workspace.
+//   k_merge    -- y = the chunks' partial sums added in chunk order.
+// No atomics take part in any sum and every sum has a fixed order, so y is
+// bitwise reproducible, and the list and layer paths give identical bits.
+// All kernels but the merge are bound by HBM bandwidth on the weight rows.
+#include "predict_device.h"
 
 namespace pi {
 namespace {
@@ -31,13 +34,6 @@ __device__ __forceinline__ float dotc<f16>(u32x4 w, u32x4 x, float acc) { return
 template <>
 __device__ __forceinline__ float dotc<float>(u32x4 w, u32x4 x, float acc) { return dot4_f32(w, x, acc); }
 
-// ---------------------------------------------------------------------------
-// up: h[j][k] = act(w_up[idx[k]] . x[j] (+ bias)), one wave per listed row.
-// ---------------------------------------------------------------------------
-constexpr int kUpThreads = 256;
-constexpr int kUpWaves = kUpThreads / kWave;
-constexpr int kUpChunks = 16;   // 16-byte chunks per lane per pass (16 KB of row per wave)
-
 template <int ACT>
 __device__ __forceinline__ float activate(float up, float gate) {
   if (ACT == ACT_REGLU) return (gate > 0.f ? gate : 0.f) * up;
@@ -45,82 +41,271 @@ __device__ __forceinline__ float activate(float up, float gate) {
   return ACT == ACT_RELU2 ? r * r : r;
 }
 
-template <typename W, int ACT, int NT>
-__global__ __launch_bounds__(kUpThreads) void k_up(const W* __restrict__ w_up, const W* __restrict__ w_gate,
-                                                   const float* __restrict__ bias, const W* __restrict__ x,
-                                                   int d, int d_ff, int nt, const int32_t* __restrict__ idx,
-                                                   const int32_t* __restrict__ count_ptr, int max_count,
-                                                   float* __restrict__ h, int ld_h) {
+// ---------------------------------------------------------------------------
+// One neuron's up projection for nt tokens, computed by a whole wave:
+// hv[j] = act(w_up[i] . x[j] (+ bias), w_gate[i] . x[j] + bias).  Lane l
+// takes 16-byte chunks l, l+64, ... of the row; sum order: lane chunk order,
+// then the wave butterfly, so every lane ends with the same hv.  x comes from
+// LDS (XL: [NT][d/E] 16-byte chunks staged by the workgroup) or from global
+// memory.
+// ---------------------------------------------------------------------------
+constexpr int kUpChunks = 16;   // chunks per lane per pass: 16 KB of row per wave
+
+template <typename W, int ACT, int NT, bool XL>
+__device__ __forceinline__ void row_up(const W* __restrict__ w_up, const W* __restrict__ w_gate, float b, int i,
+                                       int d, const char* __restrict__ xb, const u32x4* x_lds, int nt, int lane,
+                                       float (&hv)[NT]) {
   constexpr int E = 16 / sizeof(W);
   constexpr bool GATED = ACT == ACT_REGLU;
   const int nch = d / E;
-  const int lane = lane_id();
-  const char* xb = reinterpret_cast<const char*>(x);
-  // x tile in LDS when several tokens share a row; one token reads x from L2.
-  extern __shared__ u32x4 x_lds[];   // [NT][nch] when NT > 1
-  if (NT > 1) {
-    const int tot = nt * nch;
-    for (int e = threadIdx.x; e < tot; e += kUpThreads) x_lds[e] = ld16(xb + (size_t)e * 16);
-    __syncthreads();
-  }
-  int cnt = *count_ptr;
-  cnt = cnt < max_count ? cnt : max_count;
-  const int n_waves = gridDim.x * kUpWaves;
-  for (int k = blockIdx.x * kUpWaves + wave_id(); k < cnt; k += n_waves) {
-    const int i = idx[k];
-    if ((unsigned)i >= (unsigned)d_ff) {
-      // Outside the weight matrix: the list is malformed; the row adds nothing.
-      if (lane == 0)
-        for (int j = 0; j < nt; ++j) h[(size_t)j * ld_h + k] = 0.f;
-      continue;
+  const char* up = reinterpret_cast<const char*>(w_up + (size_t)i * d);
+  const char* gt = GATED ? reinterpret_cast<const char*>(w_gate + (size_t)i * d) : nullptr;
+  float au[NT], ag[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) au[j] = ag[j] = 0.f;
+  for (int pass = 0; pass < nch; pass += kWave * kUpChunks) {
+    u32x4 wu[kUpChunks], wg[GATED ? kUpChunks : 1];
+#pragma unroll
+    for (int m = 0; m < kUpChunks; ++m) {
+      const int ch = pass + lane + kWave * m;
+      const bool ok = ch < nch;
+      wu[m] = ok ? ld_nt(up + (size_t)ch * 16) : u32x4{0, 0, 0, 0};
+      if (GATED) wg[m] = ok ? ld_nt(gt + (size_t)ch * 16) : u32x4{0, 0, 0, 0};
     }
-    const char* up = reinterpret_cast<const char*>(w_up + (size_t)i * d);
-    const char* gt = GATED ? reinterpret_cast<const char*>(w_gate + (size_t)i * d) : nullptr;
-    float au[NT], ag[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) au[j] = ag[j] = 0.f;
-    for (int pass = 0; pass < nch; pass += kWave * kUpChunks) {
-      u32x4 wu[kUpChunks], wg[GATED ? kUpChunks : 1];
+    for (int j = 0; j < NT; ++j) {
+      if (j < nt) {
+        const char* xr = xb + (size_t)j * d * sizeof(W);
 #pragma unroll
-      for (int m = 0; m < kUpChunks; ++m) {
-        const int ch = pass + lane + kWave * m;
-        const bool ok = ch < nch;
-        wu[m] = ok ? ld_nt(up + (size_t)ch * 16) : u32x4{0, 0, 0, 0};
-        if (GATED) wg[m] = ok ? ld_nt(gt + (size_t)ch * 16) : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int m = 0; m < kUpChunks; ++m) {
-        const int ch = pass + lane + kWave * m;
-        if (ch < nch) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            if (j < nt) {
-              const u32x4 xv = NT > 1 ? x_lds[j * nch + ch] : ld16(xb + (size_t)ch * 16);
-              au[j] = dotc<W>(wu[m], xv, au[j]);
-              if (GATED) ag[j] = dotc<W>(wg[m], xv, ag[j]);
-            }
+        for (int m = 0; m < kUpChunks; ++m) {
+          const int ch = pass + lane + kWave * m;
+          if (ch < nch) {
+            const u32x4 xv = XL ? x_lds[j * nch + ch] : ld16(xr + (size_t)ch * 16);
+            au[j] = dotc<W>(wu[m], xv, au[j]);
+            if (GATED) ag[j] = dotc<W>(wg[m], xv, ag[j]);
           }
         }
       }
     }
-    const float b = bias ? bias[i] : 0.f;
+  }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if (j < nt) {
-        const float u = wave_sum(au[j]);
-        const float g = GATED ? wave_sum(ag[j]) : 0.f;
-        if (lane == 0) h[(size_t)j * ld_h + k] = GATED ? activate<ACT>(u, g + b) : activate<ACT>(u + b, 0.f);
-      }
+  for (int j = 0; j < NT; ++j) {
+    if (j < nt) {
+      const float u = wave_sum(au[j]);
+      const float g = GATED ? wave_sum(ag[j]) : 0.f;
+      hv[j] = GATED ? activate<ACT>(u, g + b) : activate<ACT>(u + b, 0.f);
+    } else {
+      hv[j] = 0.f;
     }
   }
 }
 
+// Stage the token tile of x ([nt][d] elements, 16-byte chunks) into LDS.
+template <typename W>
+__device__ __forceinline__ void stage_x(const char* __restrict__ xb, u32x4* x_lds, int nt, int d) {
+  const int tot = nt * (d / (16 / (int)sizeof(W)));
+  for (int e = threadIdx.x; e < tot; e += blockDim.x) x_lds[e] = ld16(xb + (size_t)e * 16);
+}
+
 // ---------------------------------------------------------------------------
-// down: part[c][j][col] = sum_{k in chunk c} h[j][k] * w_down_t[idx[k]][col]
+// k_up: list path.  h[j][k] (by list position k) for the neuron idx[k].
+// ---------------------------------------------------------------------------
+constexpr int kUpThreads = 256;
+constexpr int kUpWaves = kUpThreads / kWave;
+
+template <typename W, int ACT, int NT, bool XL>
+__global__ __launch_bounds__(kUpThreads) void k_up(const W* __restrict__ w_up, const W* __restrict__ w_gate,
+                                                   const float* __restrict__ bias, const W* __restrict__ x,
+                                                   int d, int d_ff, int nt, const int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ count_ptr, int max_count,
+                                                   float* __restrict__ h) {
+  extern __shared__ u32x4 x_lds[];   // [NT][d/E] when XL
+  const int lane = lane_id();
+  const int k_first = blockIdx.x * kUpWaves + wave_id();
+  // idx holds max_count entries, so the first entry can be fetched while the
+  // count is still in flight.
+  int i_next = k_first < max_count ? idx[k_first] : -1;
+  int cnt = *count_ptr;
+  cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
+  const char* xb = reinterpret_cast<const char*>(x);
+  if (XL) {
+    stage_x<W>(xb, x_lds, nt, d);
+    __syncthreads();
+  }
+  const int n_waves = gridDim.x * kUpWaves;
+  for (int k = k_first; k < cnt; k += n_waves) {
+    const int i = i_next;
+    i_next = k + n_waves < cnt ? idx[k + n_waves] : -1;
+    float hv[NT];
+    if ((unsigned)i < (unsigned)d_ff) {
+      row_up<W, ACT, NT, XL>(w_up, w_gate, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) hv[j] = 0.f;   // malformed entry: it adds nothing
+    }
+    if (lane == 0)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (j < nt) h[(size_t)j * d_ff + k] = hv[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_pred_up: layer path.  Predictor stage 2, up projection and compaction
+// fused.  Workgroup g owns kPURows consecutive neurons:
+//   A. every 16-lane group computes the logits of kPUSub neurons exactly as
+//      the stand-alone predictor does (their p2 loads go out before t and x
+//      are staged); a neuron is active when any token of the tile predicts it;
+//   B. the workgroup publishes its active count n_g as one atomic word that
+//      carries its own ready flag (no fence is needed: the word is the whole
+//      message);
+//   C. the active neurons are dealt round-robin to the 4 waves, each running
+//      the up projection of its share (x read from LDS); results stay in LDS;
+//   D. the workgroup sums the counts of workgroups 0 .. g-1 (published long
+//      before, in their phase B) to get its offset in the list, and writes
+//      its neurons and their h there in ascending order; the last workgroup
+//      writes the total count.
+// A workgroup only waits on workgroups with smaller indices, which are
+// dispatched before it, so the grid needs no co-residency.  The list equals
+// pi_compact's (ascending neuron numbers) and h is stored by list position,
+// so the down projection sees the same inputs on both paths.
+// status[] must be zero at launch (the first predictor stage clears it).
+// Every wait is bounded: after kSpinLimit polls the kernel moves on, so the
+// grid always drains.
+// ---------------------------------------------------------------------------
+constexpr int kPUThreads = 256;
+constexpr int kPUWaves = kPUThreads / kWave;
+constexpr int kPUSub = 2;                                             // neurons per group
+constexpr int kPURows = kPUThreads / kP2Group * kPUSub;               // 32 neurons per workgroup
+constexpr int kPULoads = 8;                                           // status loads per thread per batch
+constexpr unsigned kReady = 0x80000000u;
+constexpr int kSpinLimit = 1 << 16;
+
+template <typename W, int ACT, int NT, bool XL>
+__global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2, const float* __restrict__ c,
+                                                        const float* __restrict__ t, int rank, int d_ff,
+                                                        float theta, const W* __restrict__ w_up,
+                                                        const W* __restrict__ w_gate,
+                                                        const float* __restrict__ bias, const W* __restrict__ x,
+                                                        int d, int nt, unsigned* __restrict__ status,
+                                                        int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                                                        float* __restrict__ h) {
+  extern __shared__ float smem[];    // t tile [NT][rank], then (XL) x tile [NT][d/E] chunks
+  float* t_lds = smem;
+  u32x4* x_lds = reinterpret_cast<u32x4*>(smem + NT * rank);
+  __shared__ int act_lds[kPURows];
+  __shared__ float h_lds[NT][kPURows];
+  __shared__ int red_lds[kPUWaves];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int g = lane & (kP2Group - 1);
+  const int grp = threadIdx.x / kP2Group;                  // 0 .. 15
+  const int wg = blockIdx.x;
+  const int seg0 = wg * kPURows;
+  const char* xb = reinterpret_cast<const char*>(x);
+
+  // ---- A: logits ----
+  int rows[kPUSub];
+  bool rv[kPUSub];
+#pragma unroll
+  for (int s = 0; s < kPUSub; ++s) {
+    rows[s] = seg0 + s * (kPUThreads / kP2Group) + grp;
+    rv[s] = rows[s] < d_ff;
+  }
+  u32x4 w0[kPUSub][kP2Chunks];
+  issue_pass<W, kPUSub>(p2, rows, rv, rank, g, 0, w0);
+  stage_t(t, t_lds, nt, rank);
+  if (XL) stage_x<W>(xb, x_lds, nt, d);
+  __syncthreads();
+  float acc[kPUSub][NT];
+  finish_logits<W, NT, kPUSub>(p2, rows, rv, rank, t_lds, nt, g, w0, acc);
+  if (g == 0) {
+#pragma unroll
+    for (int s = 0; s < kPUSub; ++s) {
+      bool active = false;
+      if (rv[s]) {
+        const float cb = c[rows[s]];
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          if (j < nt) active |= (acc[s][j] + cb) > theta;
+      }
+      act_lds[rows[s] - seg0] = active ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  const unsigned long long am = __ballot(lane < kPURows && act_lds[lane < kPURows ? lane : 0] != 0);
+  const int n_g = __builtin_popcountll(am);
+
+  // ---- B: publish this workgroup's count ----
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&status[wg], kReady | (unsigned)n_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- C: up projection of the active neurons, dealt to the waves ----
+  unsigned long long bits = am;
+  for (int k = 0; bits; ++k) {
+    const int r = __builtin_ctzll(bits);
+    bits &= bits - 1;
+    if ((k & (kPUWaves - 1)) != wave) continue;
+    const int i = seg0 + r;
+    float hv[NT];
+    row_up<W, ACT, NT, XL>(w_up, w_gate, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
+    if (lane == 0)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) h_lds[j][r] = hv[j];
+  }
+
+  // ---- D: offset = sum of the earlier workgroups' counts; write the list ----
+  // Each thread reads its share of status[0 .. wg-1] kPULoads at a time, all
+  // loads of a batch in flight together.
+  int part = 0;
+  for (int p0 = 0; p0 < wg; p0 += kPUThreads * kPULoads) {
+    unsigned v[kPULoads];
+#pragma unroll
+    for (int u = 0; u < kPULoads; ++u) {
+      const int p = p0 + u * kPUThreads + (int)threadIdx.x;
+      v[u] = p < wg ? __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kReady;
+    }
+#pragma unroll
+    for (int u = 0; u < kPULoads; ++u) {
+      const int p = p0 + u * kPUThreads + (int)threadIdx.x;
+      for (int spin = 0; !(v[u] & kReady) && spin < kSpinLimit; ++spin) {
+        __builtin_amdgcn_s_sleep(2);
+        v[u] = __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      part += (int)(v[u] & ~kReady);
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+  if (lane == 0) red_lds[wave] = part;
+  __syncthreads();   // also orders the h_lds writes of phase C before their reads below
+  int off = 0;
+#pragma unroll
+  for (int w = 0; w < kPUWaves; ++w) off += red_lds[w];
+  if (wave == 0) {
+    const bool mine = lane < kPURows && ((am >> lane) & 1ull);
+    const int pos = off + __builtin_popcountll(am & ((1ull << lane) - 1ull));
+    if (mine) {
+      idx[pos] = seg0 + lane;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (j < nt) h[(size_t)j * d_ff + pos] = h_lds[j][lane];
+    }
+    if (wg == (int)gridDim.x - 1 && lane == 0) *count = off + n_g;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_down: part[c][j][col] = sum over list positions k of chunk c (in order)
+// of h[j][k] * w_down_t[idx[k]][col].  Chunk c covers positions
+// [c*cnt/C, (c+1)*cnt/C): equal shares of the active rows.  The chunk's list
+// entries and h values are staged in LDS (up to kDnPiece at a time) so the
+// row loop issues its weight loads with no dependent global load before them.
 // ---------------------------------------------------------------------------
 constexpr int kDnThreads = 512;
 constexpr int kDnWaves = kDnThreads / kWave;
-constexpr int kDnUnroll = 8;    // rows in flight per wave
+constexpr int kDnUnroll = 8;                 // rows in flight per wave
+constexpr int kDnPiece = kDnThreads;         // list entries staged per round
 
 template <typename W>
 __device__ __forceinline__ void axpy_chunk(float* acc, float hv, u32x4 w);
@@ -146,18 +331,21 @@ template <typename W, int NT>
 __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt, int d, int d_ff,
                                                      const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ count_ptr, int max_count,
-                                                     const float* __restrict__ h, int ld_h, int nt,
-                                                     int n_chunks, float* __restrict__ part) {
+                                                     const float* __restrict__ h, int nt, int n_chunks,
+                                                     float* __restrict__ part) {
   constexpr int E = 16 / sizeof(W);
   constexpr int SW = kWave * E;               // columns per slice
-  extern __shared__ float red[];              // [kDnWaves][NT][SW]
+  __shared__ float red[kDnWaves][SW];
+  __shared__ int rows_l[kDnPiece];
+  __shared__ float h_l[NT][kDnPiece];
   const int lane = lane_id();
   const int wave = wave_id();
-  const int col = blockIdx.x * SW + lane * E;
-  const bool cv = col < d;
+  const int slice = blockIdx.x;
   const int c = blockIdx.y;
+  const int col = slice * SW + lane * E;
+  const bool cv = col < d;
   int cnt = *count_ptr;
-  cnt = cnt < max_count ? cnt : max_count;
+  cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
   const int k0 = (int)(((long long)c * cnt) / n_chunks);
   const int k1 = (int)(((long long)(c + 1) * cnt) / n_chunks);
 
@@ -168,128 +356,181 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
     for (int e = 0; e < E; ++e) acc[j][e] = 0.f;
 
   const char* base = reinterpret_cast<const char*>(w_dt) + (size_t)col * sizeof(W);
-  for (int kb = k0 + wave; kb < k1; kb += kDnWaves * kDnUnroll) {
-    u32x4 v[kDnUnroll];
-    int rows[kDnUnroll];
+  for (int pb = k0; pb < k1; pb += kDnPiece) {
+    const int n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
+    if ((int)threadIdx.x < n) {
+      const int i = idx[pb + threadIdx.x];
+      rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
 #pragma unroll
-    for (int u = 0; u < kDnUnroll; ++u) {
-      const int k = kb + kDnWaves * u;
-      const int i = k < k1 ? idx[k] : -1;
-      rows[u] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
+      for (int j = 0; j < NT; ++j)
+        if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
     }
+    __syncthreads();
+    for (int jb = wave; jb < n; jb += kDnWaves * kDnUnroll) {
+      u32x4 v[kDnUnroll];
+      int rows[kDnUnroll];
 #pragma unroll
-    for (int u = 0; u < kDnUnroll; ++u)
-      v[u] = (rows[u] >= 0 && cv) ? ld_nt(base + (size_t)rows[u] * d * sizeof(W)) : u32x4{0, 0, 0, 0};
+      for (int u = 0; u < kDnUnroll; ++u) {
+        const int jj = jb + kDnWaves * u;
+        rows[u] = jj < n ? __builtin_amdgcn_readfirstlane(rows_l[jj]) : -1;
+      }
 #pragma unroll
-    for (int u = 0; u < kDnUnroll; ++u) {
-      const int k = kb + kDnWaves * u;
-      if (rows[u] >= 0) {
+      for (int u = 0; u < kDnUnroll; ++u)
+        v[u] = (rows[u] >= 0 && cv) ? ld_nt(base + (size_t)rows[u] * d * sizeof(W)) : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          if (j < nt) axpy_chunk<W>(acc[j], h[(size_t)j * ld_h + k], v[u]);
+      for (int u = 0; u < kDnUnroll; ++u) {
+        if (rows[u] >= 0) {
+          const int jj = jb + kDnWaves * u;
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            if (j < nt) axpy_chunk<W>(acc[j], h_l[j][jj], v[u]);
+        }
       }
     }
+    __syncthreads();
   }
-  // Sum the waves of this workgroup in wave order.
+
+  // Sum the 8 waves in wave order, one token at a time; write the partials.
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+  for (int j = 0; j < NT; ++j) {
+    if (j < nt) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) red[(wave * NT + j) * SW + lane * E + e] = acc[j][e];
-  __syncthreads();
-  for (int o = threadIdx.x; o < nt * SW; o += kDnThreads) {
-    const int j = o / SW, cc = o % SW;
-    const int gcol = blockIdx.x * SW + cc;
-    if (gcol < d) {
-      float s = red[j * SW + cc];
+      for (int e = 0; e < E; ++e) red[wave][lane * E + e] = acc[j][e];
+      __syncthreads();
+      for (int o = threadIdx.x; o < SW; o += kDnThreads) {
+        const int gcol = slice * SW + o;
+        if (gcol < d) {
+          float s = red[0][o];
 #pragma unroll
-      for (int w = 1; w < kDnWaves; ++w) s += red[(w * NT + j) * SW + cc];
-      part[((size_t)c * nt + j) * d + gcol] = s;
+          for (int w = 1; w < kDnWaves; ++w) s += red[w][o];
+          part[((size_t)c * nt + j) * d + gcol] = s;
+        }
+      }
+      __syncthreads();
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// merge: y[j][col] = sum_{c = 0 .. n_chunks-1} part[c][j][col]
+// k_merge: y[j][col] = sum over chunks c = 0, 1, ... of part[c][j][col], in
+// chunk order; one thread per output with up to 32 chunk loads in flight.
 // ---------------------------------------------------------------------------
-template <typename Y>
-__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, int n_chunks, int n,
-                                               Y* __restrict__ y) {
-  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+constexpr int kMgThreads = 256;
+constexpr int kMgBatch = 32;
+
+__global__ __launch_bounds__(kMgThreads) void k_merge(const float* __restrict__ part, int n_chunks, int n,
+                                                      void* __restrict__ y, int ytype) {
+  const int e = blockIdx.x * kMgThreads + threadIdx.x;
   if (e >= n) return;
-  f32x4 s = *reinterpret_cast<const f32x4*>(part + e);
-  for (int c = 1; c < n_chunks; ++c) s += *reinterpret_cast<const f32x4*>(part + (size_t)c * n + e);
-  if constexpr (sizeof(Y) == 4) {
-    *reinterpret_cast<f32x4*>(y + e) = s;
-  } else {
-    y[e] = (f16)s.x;
-    y[e + 1] = (f16)s.y;
-    y[e + 2] = (f16)s.z;
-    y[e + 3] = (f16)s.w;
+  float s = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += kMgBatch) {
+    float v[kMgBatch];
+#pragma unroll
+    for (int u = 0; u < kMgBatch; ++u) v[u] = c0 + u < n_chunks ? part[(size_t)(c0 + u) * n + e] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kMgBatch; ++u)
+      if (c0 + u < n_chunks) s += v[u];
   }
+  if (ytype == 1)
+    static_cast<f16*>(y)[e] = (f16)s;
+  else
+    static_cast<float*>(y)[e] = s;
 }
 
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
 template <typename W, int NT>
-hipError_t run_tile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
-  constexpr int E = 16 / sizeof(W);
-  const int d = a.d;
-  const W* x = static_cast<const W*>(a.x) + (size_t)t0 * d;
-  const float* bias = a.act == ACT_REGLU ? a.b_gate : a.b_up;
-  const int ld_h = a.d_ff;
-
-  // up: about 12 resident waves per CU on 256 CUs, no more than the list
-  const int max_waves = 3072;
-  int waves = a.max_count < max_waves ? a.max_count : max_waves;
-  if (waves < 1) waves = 1;
-  const int grid_up = (waves + kUpWaves - 1) / kUpWaves;
-  const size_t lds_up = NT > 1 ? (size_t)NT * (d / E) * 16 : 0;
-  const W* wu = static_cast<const W*>(a.w_up);
-  const W* wg = static_cast<const W*>(a.w_gate);
-  if (a.act == ACT_REGLU)
-    hipLaunchKernelGGL((k_up<W, ACT_REGLU, NT>), dim3(grid_up), dim3(kUpThreads), lds_up, s, wu, wg, bias, x, d,
-                       a.d_ff, nt, a.idx, a.count, a.max_count, a.h, ld_h);
-  else if (a.act == ACT_RELU2)
-    hipLaunchKernelGGL((k_up<W, ACT_RELU2, NT>), dim3(grid_up), dim3(kUpThreads), lds_up, s, wu, wg, bias, x, d,
-                       a.d_ff, nt, a.idx, a.count, a.max_count, a.h, ld_h);
-  else
-    hipLaunchKernelGGL((k_up<W, ACT_RELU, NT>), dim3(grid_up), dim3(kUpThreads), lds_up, s, wu, wg, bias, x, d,
-                       a.d_ff, nt, a.idx, a.count, a.max_count, a.h, ld_h);
+hipError_t launch_down(const SparseArgs& a, void* y, int nt, hipStream_t s) {
+  const dim3 grid(a.n_slices, a.n_chunks);
+  hipLaunchKernelGGL((k_down<W, NT>), grid, dim3(kDnThreads), 0, s, static_cast<const W*>(a.w_down_t), a.d, a.d_ff,
+                     a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-
-  constexpr int SW = kWave * E;
-  const int slices = (d + SW - 1) / SW;
-  const size_t lds_dn = (size_t)kDnWaves * NT * SW * sizeof(float);
-  hipLaunchKernelGGL((k_down<W, NT>), dim3(slices, a.n_chunks), dim3(kDnThreads), lds_dn, s,
-                     static_cast<const W*>(a.w_down_t), d, a.d_ff, a.idx, a.count, a.max_count, a.h, ld_h, nt,
-                     a.n_chunks, a.part);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const int n = nt * d;
-  const int grid_m = (n / 4 + 255) / 256;
-  if (a.ytype == 1)
-    hipLaunchKernelGGL((k_merge<f16>), dim3(grid_m), dim3(256), 0, s, a.part, a.n_chunks, n,
-                       static_cast<f16*>(a.y) + (size_t)t0 * d);
-  else
-    hipLaunchKernelGGL((k_merge<float>), dim3(grid_m), dim3(256), 0, s, a.part, a.n_chunks, n,
-                       static_cast<float*>(a.y) + (size_t)t0 * d);
+  const int n = nt * a.d;
+  hipLaunchKernelGGL(k_merge, dim3((n + kMgThreads - 1) / kMgThreads), dim3(kMgThreads), 0, s, a.part, a.n_chunks,
+                     n, y, a.ytype);
   return hipGetLastError();
 }
 
+// x is staged in LDS when its token tile fits in 32 KB.
 template <typename W>
-hipError_t run_all(const SparseArgs& a, hipStream_t s) {
-  const int tile = sparse_tile(a.wtype, a.d);
+bool x_in_lds(int nt_tmpl, int d) { return (size_t)nt_tmpl * d * sizeof(W) <= 32768; }
+
+template <typename W, int ACT, int NT>
+hipError_t launch_up(const SparseArgs& a, const W* x, int nt, hipStream_t s) {
+  const int max_waves = 3072;   // about 12 resident waves per CU on 256 CUs
+  int waves = a.max_count < max_waves ? a.max_count : max_waves;
+  if (waves < 1) waves = 1;
+  const int grid = (waves + kUpWaves - 1) / kUpWaves;
+  const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
+  const W* wu = static_cast<const W*>(a.w_up);
+  const W* wg = static_cast<const W*>(a.w_gate);
+  if (x_in_lds<W>(NT, a.d)) {
+    const size_t lds = (size_t)NT * a.d * sizeof(W);
+    hipLaunchKernelGGL((k_up<W, ACT, NT, true>), dim3(grid), dim3(kUpThreads), lds, s, wu, wg, bias, x, a.d, a.d_ff,
+                       nt, a.idx, a.count, a.max_count, a.h);
+  } else {
+    hipLaunchKernelGGL((k_up<W, ACT, NT, false>), dim3(grid), dim3(kUpThreads), 0, s, wu, wg, bias, x, a.d, a.d_ff,
+                       nt, a.idx, a.count, a.max_count, a.h);
+  }
+  return hipGetLastError();
+}
+
+template <typename W, int ACT, int NT>
+hipError_t launch_pred_up(const SparseArgs& a, const LayerArgs& L, const W* x, int nt, hipStream_t s) {
+  const int grid = layer_segments(a.d_ff);
+  const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
+  const W* p2 = static_cast<const W*>(L.p2);
+  const W* wu = static_cast<const W*>(a.w_up);
+  const W* wg = static_cast<const W*>(a.w_gate);
+  const size_t lds_t = (size_t)NT * L.rank * sizeof(float);
+  if (x_in_lds<W>(NT, a.d)) {
+    const size_t lds = lds_t + (size_t)NT * a.d * sizeof(W);
+    hipLaunchKernelGGL((k_pred_up<W, ACT, NT, true>), dim3(grid), dim3(kPUThreads), lds, s, p2, L.c, L.t, L.rank,
+                       a.d_ff, L.theta, wu, wg, bias, x, a.d, nt, L.status, L.idx, L.count, a.h);
+  } else {
+    hipLaunchKernelGGL((k_pred_up<W, ACT, NT, false>), dim3(grid), dim3(kPUThreads), lds_t, s, p2, L.c, L.t, L.rank,
+                       a.d_ff, L.theta, wu, wg, bias, x, a.d, nt, L.status, L.idx, L.count, a.h);
+  }
+  return hipGetLastError();
+}
+
+template <typename W, int NT>
+hipError_t up_dispatch(const SparseArgs& a, const LayerArgs* L, const W* x, int nt, hipStream_t s) {
+  if (L) {
+    if (a.act == ACT_REGLU) return launch_pred_up<W, ACT_REGLU, NT>(a, *L, x, nt, s);
+    if (a.act == ACT_RELU2) return launch_pred_up<W, ACT_RELU2, NT>(a, *L, x, nt, s);
+    return launch_pred_up<W, ACT_RELU, NT>(a, *L, x, nt, s);
+  }
+  if (a.act == ACT_REGLU) return launch_up<W, ACT_REGLU, NT>(a, x, nt, s);
+  if (a.act == ACT_RELU2) return launch_up<W, ACT_RELU2, NT>(a, x, nt, s);
+  return launch_up<W, ACT_RELU, NT>(a, x, nt, s);
+}
+
+template <typename W, int NT>
+hipError_t run_tile(const SparseArgs& a, const LayerArgs* L, int t0, int nt, hipStream_t s) {
+  const W* x = static_cast<const W*>(a.x) + (size_t)t0 * a.d;
+  hipError_t e = up_dispatch<W, NT>(a, L, x, nt, s);
+  if (e != hipSuccess) return e;
+  const size_t yoff = (size_t)t0 * a.d * (a.ytype == 1 ? 2 : 4);
+  return launch_down<W, NT>(a, static_cast<char*>(a.y) + yoff, nt, s);
+}
+
+template <typename W>
+hipError_t run_all(const SparseArgs& a, const LayerArgs* L, hipStream_t s) {
+  const int tile = kSparseTile;
   for (int t0 = 0; t0 < a.n_tok; t0 += tile) {
     const int nt = a.n_tok - t0 < tile ? a.n_tok - t0 : tile;
     hipError_t e;
     if (nt == 1)
-      e = run_tile<W, 1>(a, t0, nt, s);
+      e = run_tile<W, 1>(a, L, t0, nt, s);
     else if (nt == 2)
-      e = run_tile<W, 2>(a, t0, nt, s);
+      e = run_tile<W, 2>(a, L, t0, nt, s);
     else if (nt <= 4)
-      e = run_tile<W, 4>(a, t0, nt, s);
+      e = run_tile<W, 4>(a, L, t0, nt, s);
     else
-      e = run_tile<W, 8>(a, t0, nt, s);
+      e = run_tile<W, 8>(a, L, t0, nt, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -297,32 +538,28 @@ hipError_t run_all(const SparseArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int sparse_tile(int wtype, int d) {
-  // Tokens per pass: the x tile of the up kernel (tile * d * elem bytes) and
-  // the wave-sum buffer of the down kernel (8 * tile * slice * 4 bytes) must
-  // each fit in 64 KB of LDS.
-  const int eb = wtype == 1 ? 2 : 4;
-  const int E = 16 / eb;
-  int tile = 8;
-  while (tile > 1 && ((size_t)tile * d * eb > 65536 || (size_t)kDnWaves * tile * kWave * E * 4 > 65536)) tile >>= 1;
-  return tile;
-}
-
-int sparse_chunks(int wtype, int d, int d_ff, int n_tok) {
-  (void)d_ff;
-  (void)n_tok;
+void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices) {
   const int E = wtype == 1 ? 8 : 4;
   const int slices = (d + kWave * E - 1) / (kWave * E);
   // Aim for about 2048 waves (8 per CU) in the down kernel.
   int c = (2048 / kDnWaves + slices - 1) / slices;
   if (c < 1) c = 1;
   if (c > 64) c = 64;
-  return c;
+  *n_chunks = c;
+  *n_slices = slices;
 }
 
+int layer_segments(int d_ff) { return (d_ff + kPURows - 1) / kPURows; }
+
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s) {
-  if (a.wtype == 1) return run_all<f16>(a, s);
-  return run_all<float>(a, s);
+  if (a.wtype == 1) return run_all<f16>(a, nullptr, s);
+  return run_all<float>(a, nullptr, s);
+}
+
+hipError_t launch_layer_fused(const SparseArgs& a, const LayerArgs& L, hipStream_t s) {
+  // a single token tile: the caller guarantees n_tok <= kSparseTile
+  if (a.wtype == 1) return run_all<f16>(a, &L, s);
+  return run_all<float>(a, &L, s);
 }
 
 }  // namespace pi

@@ -10,17 +10,11 @@
 // Both stages are dense GEMVs at about 1 flop per byte, so they are bound by
 // HBM bandwidth: the kernels stream p1 and p2 with 16-byte non-temporal loads
 // and keep the small vectors (x, t) in L2 / LDS.  t stays in fp32.
-#include "pi_internal.h"
+#include "predict_device.h"
 
 namespace pi {
 namespace {
 
-// ---------------------------------------------------------------------------
-// Stage 1: t[n][r] = p1[r] . x[n].  One 256-thread workgroup per row of p1;
-// the row is split into 16-byte chunks, thread j taking chunks j, j+256, ...
-// Sum order: per-thread chunk order, then the wave butterfly, then waves
-// 0..3 in order -- fixed, so results are bitwise reproducible.
-// ---------------------------------------------------------------------------
 template <typename W>
 __device__ __forceinline__ float dot_chunk(u32x4 w, u32x4 x, float acc);
 template <>
@@ -28,14 +22,25 @@ __device__ __forceinline__ float dot_chunk<f16>(u32x4 w, u32x4 x, float acc) { r
 template <>
 __device__ __forceinline__ float dot_chunk<float>(u32x4 w, u32x4 x, float acc) { return dot4_f32(w, x, acc); }
 
+// ---------------------------------------------------------------------------
+// Stage 1: t[n][r] = p1[r] . x[n].  One 256-thread workgroup per row of p1;
+// the row is split into 16-byte chunks, thread j taking chunks j, j+256, ...
+// Sum order: per-thread chunk order, then the wave butterfly, then waves
+// 0..3 in order -- fixed, so results are bitwise reproducible.
+// Block 0 also clears `zero_n` words at `zero_ptr` (counters a later kernel
+// of the same call relies on); NULL skips it.
+// ---------------------------------------------------------------------------
 constexpr int kP1Threads = 256;
 constexpr int kP1Chunks = 4;   // chunks per thread per pass
 constexpr int kP1Tok = 8;      // tokens per pass over the row
 
 template <typename W>
 __global__ __launch_bounds__(kP1Threads) void k_pred1(const W* __restrict__ p1, const W* __restrict__ x,
-                                                      int n_tok, int d, int rank, float* __restrict__ t) {
+                                                      int n_tok, int d, int rank, float* __restrict__ t,
+                                                      unsigned* __restrict__ zero_ptr, int zero_n) {
   constexpr int E = 16 / sizeof(W);
+  if (zero_ptr != nullptr && blockIdx.x == 0)
+    for (int e = threadIdx.x; e < zero_n; e += kP1Threads) zero_ptr[e] = 0u;
   const int row = blockIdx.x;
   const int nch = d / E;
   const char* rowp = reinterpret_cast<const char*>(p1 + (size_t)row * d);
@@ -86,98 +91,48 @@ __global__ __launch_bounds__(kP1Threads) void k_pred1(const W* __restrict__ p1, 
 
 // ---------------------------------------------------------------------------
 // Stage 2: l[n][i] = p2[i] . t[n] + c[i]; mask = l > theta.
-// Rows of p2 are short (rank elements), so 16 lanes share a row: a wave
-// covers 4 rows per step and a 256-thread workgroup 16 rows.  Each lane
-// takes chunks g, g+16, ... of its row; the token tile of t sits in LDS.
-// Sum order: per-lane chunk order, then a 16-lane butterfly -- fixed.
+// 16 lanes share a row: a wave covers 4 rows per step and a 256-thread
+// workgroup 16 rows; the token tile of t sits in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kP2Threads = 256;
-constexpr int kP2Group = 16;                          // lanes per row
-constexpr int kP2Rows = kP2Threads / kP2Group;        // rows per workgroup step
-constexpr int kP2Chunks = 8;                          // chunks per lane per pass
-
-template <typename W>
-__device__ __forceinline__ float dot_chunk_t(u32x4 w, const float* tv, float acc);
-template <>
-__device__ __forceinline__ float dot_chunk_t<f16>(u32x4 w, const float* tv, float acc) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(tv);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(tv + 4);
-  const f16x2 h0 = as_h2(w.x), h1 = as_h2(w.y), h2 = as_h2(w.z), h3 = as_h2(w.w);
-  acc = __builtin_fmaf((float)h0.x, a.x, acc);
-  acc = __builtin_fmaf((float)h0.y, a.y, acc);
-  acc = __builtin_fmaf((float)h1.x, a.z, acc);
-  acc = __builtin_fmaf((float)h1.y, a.w, acc);
-  acc = __builtin_fmaf((float)h2.x, b.x, acc);
-  acc = __builtin_fmaf((float)h2.y, b.y, acc);
-  acc = __builtin_fmaf((float)h3.x, b.z, acc);
-  acc = __builtin_fmaf((float)h3.y, b.w, acc);
-  return acc;
-}
-template <>
-__device__ __forceinline__ float dot_chunk_t<float>(u32x4 w, const float* tv, float acc) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(tv);
-  acc = __builtin_fmaf(as_f(w.x), a.x, acc);
-  acc = __builtin_fmaf(as_f(w.y), a.y, acc);
-  acc = __builtin_fmaf(as_f(w.z), a.z, acc);
-  acc = __builtin_fmaf(as_f(w.w), a.w, acc);
-  return acc;
-}
+constexpr int kP2Rows = kP2Threads / kP2Group;   // rows per workgroup step
 
 template <typename W, int NT>
 __global__ __launch_bounds__(kP2Threads) void k_pred2(const W* __restrict__ p2, const float* __restrict__ c,
                                                       const float* __restrict__ t, int nt, int rank, int d_ff,
                                                       float theta, uint8_t* __restrict__ mask,
                                                       float* __restrict__ logits) {
-  constexpr int E = 16 / sizeof(W);
   extern __shared__ float t_lds[];   // [NT][rank]
-  // Stage the token tile of t (nt rows of rank floats) into LDS.
-  const int tot4 = nt * rank / 4;
-  for (int e = threadIdx.x; e < tot4; e += kP2Threads)
-    reinterpret_cast<f32x4*>(t_lds)[e] = reinterpret_cast<const f32x4*>(t)[e];
-  __syncthreads();
-
   const int lane = lane_id();
   const int g = lane & (kP2Group - 1);
   const int q = lane / kP2Group;
-  const int nch = rank / E;
   const int n_steps = (d_ff + kP2Rows - 1) / kP2Rows;
-  for (int step = blockIdx.x; step < n_steps; step += gridDim.x) {
-    const int row = step * kP2Rows + wave_id() * (kWave / kP2Group) + q;
-    const bool rv = row < d_ff;
-    const char* rowp = reinterpret_cast<const char*>(p2 + (size_t)(rv ? row : 0) * rank);
-    float acc[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = 0.f;
-    for (int pass = 0; pass < nch; pass += kP2Group * kP2Chunks) {
-      u32x4 w[kP2Chunks];
-#pragma unroll
-      for (int m = 0; m < kP2Chunks; ++m) {
-        const int ch = pass + g + kP2Group * m;
-        w[m] = (rv && ch < nch) ? ld_nt(rowp + (size_t)ch * 16) : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int m = 0; m < kP2Chunks; ++m) {
-        const int ch = pass + g + kP2Group * m;
-        if (ch < nch) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            if (j < nt) acc[j] = dot_chunk_t<W>(w[m], t_lds + j * rank + ch * E, acc[j]);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = group_sum<kP2Group>(acc[j]);
-    if (g == 0 && rv) {
-      const float cb = c[row];
+  int step = blockIdx.x;
+  int rows[1] = {step * kP2Rows + wave_id() * (kWave / kP2Group) + q};
+  bool rv[1] = {rows[0] < d_ff};
+  // The first step's p2 loads go out before t is staged.
+  u32x4 w0[1][kP2Chunks];
+  issue_pass<W, 1>(p2, rows, rv, rank, g, 0, w0);
+  stage_t(t, t_lds, nt, rank);
+  __syncthreads();
+  while (step < n_steps) {
+    float acc[1][NT];
+    finish_logits<W, NT, 1>(p2, rows, rv, rank, t_lds, nt, g, w0, acc);
+    if (g == 0 && rv[0]) {
+      const float cb = c[rows[0]];
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         if (j < nt) {
-          const float l = acc[j] + cb;
-          mask[(size_t)j * d_ff + row] = (l > theta) ? 1 : 0;
-          if (logits) logits[(size_t)j * d_ff + row] = l;
+          const float l = acc[0][j] + cb;
+          mask[(size_t)j * d_ff + rows[0]] = (l > theta) ? 1 : 0;
+          if (logits) logits[(size_t)j * d_ff + rows[0]] = l;
         }
       }
     }
+    step += gridDim.x;
+    rows[0] = step * kP2Rows + wave_id() * (kWave / kP2Group) + q;
+    rv[0] = step < n_steps && rows[0] < d_ff;
+    if (step < n_steps) issue_pass<W, 1>(p2, rows, rv, rank, g, 0, w0);
   }
 }
 
@@ -195,9 +150,7 @@ hipError_t launch_pred2_tile(const W* p2, const float* c, const float* t, int nt
 template <typename W>
 hipError_t pred2_all(const W* p2, const float* c, const float* t, int n_tok, int rank, int d_ff, float theta,
                      uint8_t* mask, float* logits, hipStream_t s) {
-  // Token tiles share one pass over p2; a tile of t must fit 64 KB of LDS.
-  int tile = 8;
-  while (tile > 1 && tile * rank > 16384) tile >>= 1;
+  const int tile = pred_tile(rank);
   for (int t0 = 0; t0 < n_tok; t0 += tile) {
     const int nt = n_tok - t0 < tile ? n_tok - t0 : tile;
     const float* tt = t + (size_t)t0 * rank;
@@ -219,14 +172,22 @@ hipError_t pred2_all(const W* p2, const float* c, const float* t, int n_tok, int
 
 }  // namespace
 
+int pred_tile(int rank) {
+  // A token tile of t must fit 64 KB of LDS.
+  int tile = 8;
+  while (tile > 1 && tile * rank > 16384) tile >>= 1;
+  return tile;
+}
+
 hipError_t launch_predict_stage1(int wtype, const void* p1, const void* x, int n_tok, int d, int rank, float* t,
-                                 hipStream_t s) {
+                                 unsigned* zero_ptr, int zero_n, hipStream_t s) {
+  const int grid = rank;
   if (wtype == 1)
-    hipLaunchKernelGGL((k_pred1<f16>), dim3(rank), dim3(kP1Threads), 0, s, static_cast<const f16*>(p1),
-                       static_cast<const f16*>(x), n_tok, d, rank, t);
+    hipLaunchKernelGGL((k_pred1<f16>), dim3(grid), dim3(kP1Threads), 0, s, static_cast<const f16*>(p1),
+                       static_cast<const f16*>(x), n_tok, d, rank, t, zero_ptr, zero_n);
   else
-    hipLaunchKernelGGL((k_pred1<float>), dim3(rank), dim3(kP1Threads), 0, s, static_cast<const float*>(p1),
-                       static_cast<const float*>(x), n_tok, d, rank, t);
+    hipLaunchKernelGGL((k_pred1<float>), dim3(grid), dim3(kP1Threads), 0, s, static_cast<const float*>(p1),
+                       static_cast<const float*>(x), n_tok, d, rank, t, zero_ptr, zero_n);
   return hipGetLastError();
 }
 

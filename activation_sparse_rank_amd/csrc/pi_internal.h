@@ -82,18 +82,24 @@ enum : int { ACT_RELU = 0, ACT_REGLU = 1, ACT_RELU2 = 2 };
 // Host launchers (each returns the hipError_t of its launch)
 // ---------------------------------------------------------------------------
 
-// t[n][r] = p1[r] . x[n]           (fp32 out)
+// t[n][r] = p1[r] . x[n]  (fp32 out).  Block 0 also zeroes zero_n words at
+// zero_ptr (NULL: none), for counters a later kernel of the same call uses.
 hipError_t launch_predict_stage1(int wtype, const void* p1, const void* x, int n_tok, int d,
-                                 int rank, float* t, hipStream_t s);
+                                 int rank, float* t, unsigned* zero_ptr, int zero_n, hipStream_t s);
 // l[n][i] = p2[i] . t[n] + c[i];  mask[n][i] = l > theta
 hipError_t launch_predict_stage2(int wtype, const void* p2, const float* c, const float* t,
                                  int n_tok, int rank, int d_ff, float theta, uint8_t* mask,
                                  float* logits, hipStream_t s);
+// Tokens per pass of the predictor's second stage (a tile of t fits in LDS).
+int pred_tile(int rank);
 // ascending list of neurons marked by any token
 hipError_t launch_compact(const uint8_t* mask, int n_tok, int d_ff, int32_t* idx, int32_t* count,
                           hipStream_t s);
 
-// Sparse FFN (one call = all launches for n_tok tokens).
+// Sparse FFN (one call = all launches for n_tok tokens, in tiles of
+// kSparseTile tokens).
+constexpr int kSparseTile = 8;
+
 struct SparseArgs {
   int wtype, act, d, d_ff, n_tok, max_count;
   const void* w_up;
@@ -102,20 +108,37 @@ struct SparseArgs {
   const float* b_up;
   const float* b_gate;
   const void* x;
-  const int32_t* idx;
-  const int32_t* count;
+  const int32_t* idx;       // list of active neurons (at least max_count entries)
+  const int32_t* count;     // device count of valid list entries
   void* y;
   int ytype;
-  float* h;        // workspace [n_tok][d_ff] fp32
-  float* part;     // workspace [n_chunks][n_tok][d] fp32
-  int n_chunks;
+  float* h;                 // workspace [kSparseTile][d_ff] fp32, by neuron number
+  float* part;              // workspace [n_chunks][kSparseTile][d] fp32
+  int n_chunks, n_slices;
 };
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
 
-// Partial-sum chunk count and tokens per pass used for a given shape (they
-// size the workspace).
-int sparse_chunks(int wtype, int d, int d_ff, int n_tok);
-int sparse_tile(int wtype, int d);
+// Predictor operands of the fused layer path (one token tile): stage 2 of
+// the predictor, the compaction and the up projection run as one kernel
+// that writes the list (idx, count) the down projection reads.
+struct LayerArgs {
+  const void* p2;
+  const float* c;
+  const float* t;           // [n_tok][rank] from stage 1
+  int rank;
+  float theta;
+  unsigned* status;         // workspace [layer_segments(d_ff)], zero at launch
+  int32_t* idx;             // workspace [d_ff]
+  int32_t* count;           // workspace, one int
+};
+// n_tok <= min(kSparseTile, pred_tile(rank)); a.idx / a.count must be L.idx / L.count.
+hipError_t launch_layer_fused(const SparseArgs& a, const LayerArgs& L, hipStream_t s);
+// Number of neuron segments (workgroups) of the fused kernel.
+int layer_segments(int d_ff);
+
+// How the down projection splits the active list (n_chunks chunks) and the
+// columns (n_slices slices); sizes the workspace.
+void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices);
 
 hipError_t launch_q4_0_repack(const void* src, int rows, int cols, void* dst, hipStream_t s);
 
