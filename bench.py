@@ -8,10 +8,13 @@ graph that reads its inputs from a staging buffer; each step copies that
 token's inputs (one vector per layer, already in HBM) into the staging buffer
 and replays the graph.
 
-Printed: one JSON line with layer-tokens/s (tokens x layers / wall time),
-a roofline entry for the dominant ABI call (algorithmic bytes per call over
-its event-timed average duration, against the 8 TB/s HBM peak), and the CPU
-oracle timed on a bounded sample of the same workload.
+Printed: one JSON line with layer-tokens/s (tokens x layers / wall time);
+a roofline entry for the layer call (pi_layer: algorithmic bytes per call --
+predictor weights, the active FFN rows, biases, list and vectors -- over its
+event-timed average duration, against the 8 TB/s HBM peak), the same for the
+gather path alone (pi_sparse_ffn) and the predictor alone (pi_predict), each
+timed in its own graph over all layers; and the CPU oracle timed on a
+bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload falcon40b]
 """
@@ -59,6 +62,16 @@ def bytes_active(cfg, cnt):
     return cnt * cfg.n_mat * _row_bytes(cfg)
 
 
+def bytes_layer(cfg, cnt):
+    """Algorithmic bytes of one pi_layer call at batch 1: both predictor
+    matrices and its bias, x, the active FFN rows with their biases, the
+    active list and y."""
+    eb = ELEM_BYTES[cfg.pred_wtype]
+    xb = 2 if cfg.wtype == "q4_0" else ELEM_BYTES[cfg.wtype]
+    return ((cfg.rank * cfg.d_model + cfg.d_ff * cfg.rank) * eb + 4 * cfg.d_ff + cfg.d_model * xb
+            + bytes_active(cfg, cnt) + 8 * cnt + 4 * cfg.d_model)
+
+
 def _time_graph(graph, reps, stream):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -72,7 +85,7 @@ def _time_graph(graph, reps, stream):
     return start.elapsed_time(end) / reps          # ms per replay
 
 
-def cpu_baseline(cfg, layers, xs_host, budget_s=15.0, max_samples=16):
+def cpu_baseline(cfg, layers, xs_host, budget_s=20.0, max_samples=64):
     """The oracle's layer() on host copies of a few layers and tokens."""
     import oracle
     try:
@@ -142,7 +155,8 @@ def main(argv=None):
         lw = workload.make_layer(cfg, li, dev, args.seed)
         lw.pop("p")
         layers.append(lw)
-        print(f"[bench] generated layer {li + 1}/{L}", file=sys.stderr, flush=True) if (li + 1) % 10 == 0 else None
+        if (li + 1) % 10 == 0:
+            print(f"[bench] generated layer {li + 1}/{L}", file=sys.stderr, flush=True)
     x_all = torch.empty((T, L, d), dtype=xdt, device=dev)
     for li in range(L):
         x_all[:, li] = workload.make_tokens(cfg, li, T, dev, args.seed)
@@ -238,6 +252,10 @@ def main(argv=None):
                 "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                 "bytes_per_launch": int(b), "avg_launch_us": round(ms * 1e3, 3)}
 
+    # whole-layer bytes per layer-token, averaged over the timed steps
+    b_layer = float(np.mean([bytes_layer(cfg, c) for c in counts.flat]))
+    ms_layer = ms_step / L
+    layer_roof = roof("pi_layer (k_pred1 + k_pred_up + k_down + k_merge)", b_layer, ms_layer)
     parts = {
         "predict": roof("pi_predict (k_pred1 + k_pred2)", b_pred, ms_pred),
         "compact": {"kernel": "pi_compact (k_compact)", "avg_launch_us": round(ms_comp * 1e3, 3),
@@ -245,11 +263,8 @@ def main(argv=None):
         "gather": roof("pi_sparse_ffn (k_up + k_down + k_merge)", b_sp, ms_sp),
     }
     parts["gather"]["active_weight_gbps"] = round(b_act / (ms_sp * 1e-3) / 1e9, 1)
-    dominant = "gather" if ms_sp >= ms_pred else "predict"
+    parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
 
-    # whole-layer bytes per layer-token, averaged over the timed steps
-    b_layer = float(np.mean([bytes_predict(cfg) + bytes_compact(cfg, c) + bytes_gather(cfg, c)
-                             for c in counts.flat]))
     out = {
         "metric": METRIC,
         "value": round(layer_tok_s, 1),
@@ -266,9 +281,8 @@ def main(argv=None):
         "config": {"workload": f"{cfg.name} decode batch 1", "d_model": d, "d_ff": f, "layers": L,
                    "rank": cfg.rank, "act": cfg.act, "weights": cfg.wtype, "mean_density": cfg.rho,
                    "parallelism": "none (1 GPU)"},
-        "roofline": parts[dominant],
+        "roofline": layer_roof,
         "roofline_parts": parts,
-        "layer_hbm_gbps_all_bytes": round(b_layer * args.steps * L / (ms_total * 1e-3) / 1e9, 1),
         "count_mean": round(cnt_mean, 1),
         "count_min": int(counts.min()),
         "count_max": int(counts.max()),
@@ -277,7 +291,7 @@ def main(argv=None):
 
     if not args.no_cpu_baseline:
         import oracle  # noqa: F401  (the baseline leg is the only user of the oracle here)
-        n_base_layers, n_base_tok = 2, 4
+        n_base_layers, n_base_tok = 4, 16
         host_layers = []
         for li in range(n_base_layers):
             lw = layers[li]
