@@ -47,7 +47,6 @@ pi_status check_ffn(const pi_ffn* f) {
   if (f->act == PI_REGLU && !al16(f->w_gate)) return PI_E_ALIGN;
   if (f->b_up && !al16(f->b_up)) return PI_E_ALIGN;
   if (f->b_gate && !al16(f->b_gate)) return PI_E_ALIGN;
-  if (f->wtype == PI_Q4_0) return PI_E_DTYPE;   // Q4_0 compute kernels not available yet
   return PI_OK;
 }
 
@@ -78,7 +77,8 @@ Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
     L.status = take((size_t)L.n_segments * sizeof(unsigned));
   }
   if (ffn) {
-    const int nt = n_tok < pi::kSparseTile ? n_tok : pi::kSparseTile;
+    const int tile = pi::sparse_tile(ffn->wtype, ffn->d_model);
+    const int nt = n_tok < tile ? n_tok : tile;
     pi::sparse_chunking(ffn->wtype, ffn->d_model, &L.n_chunks, &L.n_slices);
     L.h = take((size_t)nt * ffn->d_ff * sizeof(float));
     L.part = take((size_t)L.n_chunks * nt * ffn->d_model * sizeof(float));
@@ -218,7 +218,7 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
   unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   const hipStream_t s = as_stream(stream);
   pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
-  const bool fused = n_tok <= pi::kSparseTile && n_tok <= pi::pred_tile(pred->rank);
+  const bool fused = n_tok <= pi::sparse_tile(ffn->wtype, ffn->d_model) && n_tok <= pi::pred_tile(pred->rank);
   // Stage 1 also clears the fused kernel's segment counters.
   hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t,
                                            fused ? status : nullptr, fused ? L.n_segments : 0, s);

@@ -22,6 +22,8 @@
 // No atomics take part in any sum and every sum has a fixed order, so y is
 // bitwise reproducible, and the list and layer paths give identical bits.
 // All kernels but the merge are bound by HBM bandwidth on the weight rows.
+#include <type_traits>
+
 #include "predict_device.h"
 
 namespace pi {
@@ -108,17 +110,124 @@ __device__ __forceinline__ void stage_x(const char* __restrict__ xb, u32x4* x_ld
 }
 
 // ---------------------------------------------------------------------------
+// Q4_0 rows.  A row of d weights is d/32 blocks; block b has a 16-byte code
+// group (at codes + (row*nb + b)*16) and an fp16 scale (at scales +
+// (row*nb + b)*2), in the repacked layout of k_q4.hip.  Word k, slot u of a
+// code group holds the codes of the weight pair (8k+2u, 8k+2u+1); OR-ing the
+// two 4-bit codes into the mantissas of 1024.0 and subtracting 1032.0 gives
+// the exact fp16 pair (q-8, q'-8), which v_dot2_f32_f16 multiplies with the
+// matching pair of activations.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f16x2 q4_pair(unsigned w, int u) {
+  const unsigned bits = ((w >> (4 * u)) & 0x000F000Fu) | 0x64006400u;
+  return as_h2(bits) - f16x2{(f16)1032.0f, (f16)1032.0f};
+}
+
+// sum over one block of (q-8) * x in fp32 (exact fp16 products); xq are the
+// block's four 16-byte chunks of activations.
+__device__ __forceinline__ float dot_q4(u32x4 cw, const u32x4 (&xq)[4]) {
+  float acc = 0.f;
+  const unsigned w[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned xw[4] = {xq[k].x, xq[k].y, xq[k].z, xq[k].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_fdot2(q4_pair(w[k], u), as_h2(xw[u]), acc, false);
+  }
+  return acc;
+}
+
+constexpr int kUpBlocks = 8;   // Q4 blocks per lane per pass (512 blocks = 16384 weights per pass)
+
+// One neuron's up projection with Q4_0 weights; same structure and sum order
+// rules as row_up: lane l takes blocks l, l+64, ...; each block's sum is
+// scaled by its fp16 scale and added in block order; then the wave butterfly.
+template <int ACT, int NT, bool XL>
+__device__ __forceinline__ void row_up_q4(const uint8_t* __restrict__ w_up, const uint8_t* __restrict__ w_gate,
+                                          size_t scale_off, float b, int i, int d, const char* __restrict__ xb,
+                                          const u32x4* x_lds, int nt, int lane, float (&hv)[NT]) {
+  constexpr bool GATED = ACT == ACT_REGLU;
+  const int nb = d / 32;
+  const int nch = d / 8;                       // 16-byte activation chunks per token
+  const uint8_t* cu = w_up + (size_t)i * nb * 16;
+  const f16* su = reinterpret_cast<const f16*>(w_up + scale_off) + (size_t)i * nb;
+  const uint8_t* cg = GATED ? w_gate + (size_t)i * nb * 16 : nullptr;
+  const f16* sg = GATED ? reinterpret_cast<const f16*>(w_gate + scale_off) + (size_t)i * nb : nullptr;
+  float au[NT], ag[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) au[j] = ag[j] = 0.f;
+  for (int pass = 0; pass < nb; pass += kWave * kUpBlocks) {
+    u32x4 wu[kUpBlocks], wg[GATED ? kUpBlocks : 1];
+    float du[kUpBlocks], dg[GATED ? kUpBlocks : 1];
+#pragma unroll
+    for (int m = 0; m < kUpBlocks; ++m) {
+      const int blk = pass + lane + kWave * m;
+      const bool ok = blk < nb;
+      wu[m] = ok ? ld_nt(cu + (size_t)blk * 16) : u32x4{0, 0, 0, 0};
+      du[m] = ok ? (float)su[blk] : 0.f;
+      if (GATED) {
+        wg[m] = ok ? ld_nt(cg + (size_t)blk * 16) : u32x4{0, 0, 0, 0};
+        dg[m] = ok ? (float)sg[blk] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (j < nt) {
+        const char* xr = xb + (size_t)j * d * sizeof(f16);
+#pragma unroll
+        for (int m = 0; m < kUpBlocks; ++m) {
+          const int blk = pass + lane + kWave * m;
+          if (blk < nb) {
+            u32x4 xq[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              xq[k] = XL ? x_lds[j * nch + 4 * blk + k] : ld16(xr + (size_t)(4 * blk + k) * 16);
+            au[j] = __builtin_fmaf(du[m], dot_q4(wu[m], xq), au[j]);
+            if (GATED) ag[j] = __builtin_fmaf(dg[m], dot_q4(wg[m], xq), ag[j]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (j < nt) {
+      const float u = wave_sum(au[j]);
+      const float g = GATED ? wave_sum(ag[j]) : 0.f;
+      hv[j] = GATED ? activate<ACT>(u, g + b) : activate<ACT>(u + b, 0.f);
+    } else {
+      hv[j] = 0.f;
+    }
+  }
+}
+
+// Up projection of neuron i for any FFN weight type.
+template <typename WF, int ACT, int NT, bool XL>
+__device__ __forceinline__ void row_up_any(const void* w_up, const void* w_gate, size_t scale_off, float b, int i,
+                                           int d, const char* xb, const u32x4* x_lds, int nt, int lane,
+                                           float (&hv)[NT]) {
+  if constexpr (std::is_same<WF, Q4>::value)
+    row_up_q4<ACT, NT, XL>(static_cast<const uint8_t*>(w_up), static_cast<const uint8_t*>(w_gate), scale_off, b, i,
+                           d, xb, x_lds, nt, lane, hv);
+  else
+    row_up<WF, ACT, NT, XL>(static_cast<const WF*>(w_up), static_cast<const WF*>(w_gate), b, i, d, xb, x_lds, nt,
+                            lane, hv);
+}
+
+// ---------------------------------------------------------------------------
 // k_up: list path.  h[j][k] (by list position k) for the neuron idx[k].
 // ---------------------------------------------------------------------------
 constexpr int kUpThreads = 256;
 constexpr int kUpWaves = kUpThreads / kWave;
 
-template <typename W, int ACT, int NT, bool XL>
-__global__ __launch_bounds__(kUpThreads) void k_up(const W* __restrict__ w_up, const W* __restrict__ w_gate,
-                                                   const float* __restrict__ bias, const W* __restrict__ x,
+template <typename WF, int ACT, int NT, bool XL>
+__global__ __launch_bounds__(kUpThreads) void k_up(const void* __restrict__ w_up, const void* __restrict__ w_gate,
+                                                   size_t scale_off, const float* __restrict__ bias,
+                                                   const typename FfnTraits<WF>::X* __restrict__ x,
                                                    int d, int d_ff, int nt, const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ count_ptr, int max_count,
                                                    float* __restrict__ h) {
+  using X = typename FfnTraits<WF>::X;
   extern __shared__ u32x4 x_lds[];   // [NT][d/E] when XL
   const int lane = lane_id();
   const int k_first = blockIdx.x * kUpWaves + wave_id();
@@ -129,7 +238,7 @@ __global__ __launch_bounds__(kUpThreads) void k_up(const W* __restrict__ w_up, c
   cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
   const char* xb = reinterpret_cast<const char*>(x);
   if (XL) {
-    stage_x<W>(xb, x_lds, nt, d);
+    stage_x<X>(xb, x_lds, nt, d);
     __syncthreads();
   }
   const int n_waves = gridDim.x * kUpWaves;
@@ -138,7 +247,7 @@ __global__ __launch_bounds__(kUpThreads) void k_up(const W* __restrict__ w_up, c
     i_next = k + n_waves < cnt ? idx[k + n_waves] : -1;
     float hv[NT];
     if ((unsigned)i < (unsigned)d_ff) {
-      row_up<W, ACT, NT, XL>(w_up, w_gate, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
+      row_up_any<WF, ACT, NT, XL>(w_up, w_gate, scale_off, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
     } else {
 #pragma unroll
       for (int j = 0; j < NT; ++j) hv[j] = 0.f;   // malformed entry: it adds nothing
@@ -181,11 +290,11 @@ constexpr int kPULoads = 8;                                           // status 
 constexpr unsigned kReady = 0x80000000u;
 constexpr int kSpinLimit = 1 << 16;
 
-template <typename W, int ACT, int NT, bool XL>
+template <typename W, typename WF, int ACT, int NT, bool XL>
 __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2, const float* __restrict__ c,
                                                         const float* __restrict__ t, int rank, int d_ff,
-                                                        float theta, const W* __restrict__ w_up,
-                                                        const W* __restrict__ w_gate,
+                                                        float theta, const void* __restrict__ w_up,
+                                                        const void* __restrict__ w_gate, size_t scale_off,
                                                         const float* __restrict__ bias, const W* __restrict__ x,
                                                         int d, int nt, unsigned* __restrict__ status,
                                                         int32_t* __restrict__ idx, int32_t* __restrict__ count,
@@ -248,7 +357,7 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
     if ((k & (kPUWaves - 1)) != wave) continue;
     const int i = seg0 + r;
     float hv[NT];
-    row_up<W, ACT, NT, XL>(w_up, w_gate, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
+    row_up_any<WF, ACT, NT, XL>(w_up, w_gate, scale_off, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
     if (lane == 0)
 #pragma unroll
       for (int j = 0; j < NT; ++j) h_lds[j][r] = hv[j];
@@ -412,6 +521,120 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
 }
 
 // ---------------------------------------------------------------------------
+// k_down_q4: the down projection with Q4_0 weights.  A lane owns half a block
+// (16 columns, 8 bytes of codes) of each row, so a wave covers 1024 columns;
+// otherwise as k_down (chunks of the list, rows staged in LDS, 8 waves summed
+// in wave order).  Per row: s = h * d_block, then acc[col] += s * (q - 8).
+// ---------------------------------------------------------------------------
+constexpr int kDqUnroll = 16;               // rows in flight per wave
+constexpr int kDqCols = 16;                 // columns per lane
+constexpr int kDqSW = kWave * kDqCols;      // 1024 columns per slice
+
+template <int NT>
+__global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restrict__ w_dt, size_t scale_off, int d,
+                                                        int d_ff, const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ count_ptr, int max_count,
+                                                        const float* __restrict__ h, int nt, int n_chunks,
+                                                        float* __restrict__ part) {
+  __shared__ float red[kDnWaves][kWave * 8];
+  __shared__ int rows_l[kDnPiece];
+  __shared__ float h_l[NT][kDnPiece];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int slice = blockIdx.x;
+  const int c = blockIdx.y;
+  const int nb = d / 32;
+  const int col = slice * kDqSW + lane * kDqCols;     // first of this lane's 16 columns
+  const bool cv = col < d;
+  const int blk = col / 32, half = (col / 16) & 1;
+  const uint8_t* code_base = w_dt + (size_t)blk * 16 + half * 8;
+  const f16* scale_base = reinterpret_cast<const f16*>(w_dt + scale_off) + blk;
+  int cnt = *count_ptr;
+  cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
+  const int k0 = (int)(((long long)c * cnt) / n_chunks);
+  const int k1 = (int)(((long long)(c + 1) * cnt) / n_chunks);
+
+  float acc[NT][kDqCols];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int e = 0; e < kDqCols; ++e) acc[j][e] = 0.f;
+
+  for (int pb = k0; pb < k1; pb += kDnPiece) {
+    const int n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
+    if ((int)threadIdx.x < n) {
+      const int i = idx[pb + threadIdx.x];
+      rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
+    }
+    __syncthreads();
+    for (int jb = wave; jb < n; jb += kDnWaves * kDqUnroll) {
+      u32x2 v[kDqUnroll];
+      float dsc[kDqUnroll];
+      int rows[kDqUnroll];
+#pragma unroll
+      for (int u = 0; u < kDqUnroll; ++u) {
+        const int jj = jb + kDnWaves * u;
+        rows[u] = jj < n ? __builtin_amdgcn_readfirstlane(rows_l[jj]) : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kDqUnroll; ++u) {
+        const bool ok = rows[u] >= 0 && cv;
+        v[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(code_base + (size_t)rows[u] * nb * 16))
+                  : u32x2{0, 0};
+        dsc[u] = ok ? (float)scale_base[(size_t)rows[u] * nb] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kDqUnroll; ++u) {
+        if (rows[u] >= 0) {
+          const int jj = jb + kDnWaves * u;
+          const unsigned wd[2] = {v[u].x, v[u].y};
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            if (j < nt) {
+              const float sc = h_l[j][jj] * dsc[u];
+#pragma unroll
+              for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const f16x2 pr = q4_pair(wd[k], q);
+                  acc[j][8 * k + 2 * q] = __builtin_fmaf(sc, (float)pr.x, acc[j][8 * k + 2 * q]);
+                  acc[j][8 * k + 2 * q + 1] = __builtin_fmaf(sc, (float)pr.y, acc[j][8 * k + 2 * q + 1]);
+                }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Sum the 8 waves in wave order, 8 columns per lane per round; write the partials.
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (j < nt) {
+#pragma unroll
+      for (int r = 0; r < kDqCols / 8; ++r) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = acc[j][8 * r + e];
+        __syncthreads();
+        const int o = threadIdx.x;                      // 512 entries: lane o/8, column 8r + o%8
+        const int gcol = slice * kDqSW + (o / 8) * kDqCols + 8 * r + (o % 8);
+        if (gcol < d) {
+          float sum = red[0][o];
+#pragma unroll
+          for (int w = 1; w < kDnWaves; ++w) sum += red[w][o];
+          part[((size_t)c * nt + j) * d + gcol] = sum;
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_merge: y[j][col] = sum over chunks c = 0, 1, ... of part[c][j][col], in
 // chunk order; one thread per output with up to 32 chunk loads in flight.
 // ---------------------------------------------------------------------------
@@ -440,11 +663,25 @@ __global__ __launch_bounds__(kMgThreads) void k_merge(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-template <typename W, int NT>
+template <typename WF>
+constexpr int slice_cols() {
+  return std::is_same<WF, Q4>::value ? kDqSW : kWave * (16 / (int)sizeof(WF));
+}
+
+template <typename WF>
+size_t scale_offset(const SparseArgs& a) {
+  return std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
+}
+
+template <typename WF, int NT>
 hipError_t launch_down(const SparseArgs& a, void* y, int nt, hipStream_t s) {
   const dim3 grid(a.n_slices, a.n_chunks);
-  hipLaunchKernelGGL((k_down<W, NT>), grid, dim3(kDnThreads), 0, s, static_cast<const W*>(a.w_down_t), a.d, a.d_ff,
-                     a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
+  if constexpr (std::is_same<WF, Q4>::value)
+    hipLaunchKernelGGL((k_down_q4<NT>), grid, dim3(kDnThreads), 0, s, static_cast<const uint8_t*>(a.w_down_t),
+                       scale_offset<WF>(a), a.d, a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
+  else
+    hipLaunchKernelGGL((k_down<WF, NT>), grid, dim3(kDnThreads), 0, s, static_cast<const WF*>(a.w_down_t), a.d,
+                       a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = nt * a.d;
@@ -454,93 +691,117 @@ hipError_t launch_down(const SparseArgs& a, void* y, int nt, hipStream_t s) {
 }
 
 // x is staged in LDS when its token tile fits in 32 KB.
-template <typename W>
-bool x_in_lds(int nt_tmpl, int d) { return (size_t)nt_tmpl * d * sizeof(W) <= 32768; }
+template <typename X>
+bool x_in_lds(int nt_tmpl, int d) { return (size_t)nt_tmpl * d * sizeof(X) <= 32768; }
 
-template <typename W, int ACT, int NT>
-hipError_t launch_up(const SparseArgs& a, const W* x, int nt, hipStream_t s) {
+template <typename WF, int ACT, int NT>
+hipError_t launch_up(const SparseArgs& a, const typename FfnTraits<WF>::X* x, int nt, hipStream_t s) {
+  using X = typename FfnTraits<WF>::X;
   const int max_waves = 3072;   // about 12 resident waves per CU on 256 CUs
   int waves = a.max_count < max_waves ? a.max_count : max_waves;
   if (waves < 1) waves = 1;
   const int grid = (waves + kUpWaves - 1) / kUpWaves;
   const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
-  const W* wu = static_cast<const W*>(a.w_up);
-  const W* wg = static_cast<const W*>(a.w_gate);
-  if (x_in_lds<W>(NT, a.d)) {
-    const size_t lds = (size_t)NT * a.d * sizeof(W);
-    hipLaunchKernelGGL((k_up<W, ACT, NT, true>), dim3(grid), dim3(kUpThreads), lds, s, wu, wg, bias, x, a.d, a.d_ff,
-                       nt, a.idx, a.count, a.max_count, a.h);
+  const size_t so = scale_offset<WF>(a);
+  if (x_in_lds<X>(NT, a.d)) {
+    const size_t lds = (size_t)NT * a.d * sizeof(X);
+    hipLaunchKernelGGL((k_up<WF, ACT, NT, true>), dim3(grid), dim3(kUpThreads), lds, s, a.w_up, a.w_gate, so, bias,
+                       x, a.d, a.d_ff, nt, a.idx, a.count, a.max_count, a.h);
   } else {
-    hipLaunchKernelGGL((k_up<W, ACT, NT, false>), dim3(grid), dim3(kUpThreads), 0, s, wu, wg, bias, x, a.d, a.d_ff,
-                       nt, a.idx, a.count, a.max_count, a.h);
+    hipLaunchKernelGGL((k_up<WF, ACT, NT, false>), dim3(grid), dim3(kUpThreads), 0, s, a.w_up, a.w_gate, so, bias,
+                       x, a.d, a.d_ff, nt, a.idx, a.count, a.max_count, a.h);
   }
   return hipGetLastError();
 }
 
-template <typename W, int ACT, int NT>
-hipError_t launch_pred_up(const SparseArgs& a, const LayerArgs& L, const W* x, int nt, hipStream_t s) {
+template <typename WF, int ACT, int NT>
+hipError_t launch_pred_up(const SparseArgs& a, const LayerArgs& L, const typename FfnTraits<WF>::X* x, int nt,
+                          hipStream_t s) {
+  using X = typename FfnTraits<WF>::X;   // also the predictor's weight type
   const int grid = layer_segments(a.d_ff);
   const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
-  const W* p2 = static_cast<const W*>(L.p2);
-  const W* wu = static_cast<const W*>(a.w_up);
-  const W* wg = static_cast<const W*>(a.w_gate);
+  const X* p2 = static_cast<const X*>(L.p2);
+  const size_t so = scale_offset<WF>(a);
   const size_t lds_t = (size_t)NT * L.rank * sizeof(float);
-  if (x_in_lds<W>(NT, a.d)) {
-    const size_t lds = lds_t + (size_t)NT * a.d * sizeof(W);
-    hipLaunchKernelGGL((k_pred_up<W, ACT, NT, true>), dim3(grid), dim3(kPUThreads), lds, s, p2, L.c, L.t, L.rank,
-                       a.d_ff, L.theta, wu, wg, bias, x, a.d, nt, L.status, L.idx, L.count, a.h);
+  if (x_in_lds<X>(NT, a.d)) {
+    const size_t lds = lds_t + (size_t)NT * a.d * sizeof(X);
+    hipLaunchKernelGGL((k_pred_up<X, WF, ACT, NT, true>), dim3(grid), dim3(kPUThreads), lds, s, p2, L.c, L.t, L.rank,
+                       a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.status, L.idx, L.count, a.h);
   } else {
-    hipLaunchKernelGGL((k_pred_up<W, ACT, NT, false>), dim3(grid), dim3(kPUThreads), lds_t, s, p2, L.c, L.t, L.rank,
-                       a.d_ff, L.theta, wu, wg, bias, x, a.d, nt, L.status, L.idx, L.count, a.h);
+    hipLaunchKernelGGL((k_pred_up<X, WF, ACT, NT, false>), dim3(grid), dim3(kPUThreads), lds_t, s, p2, L.c, L.t,
+                       L.rank, a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.status, L.idx, L.count,
+                       a.h);
   }
   return hipGetLastError();
 }
 
-template <typename W, int NT>
-hipError_t up_dispatch(const SparseArgs& a, const LayerArgs* L, const W* x, int nt, hipStream_t s) {
+template <typename WF, int NT>
+hipError_t up_dispatch(const SparseArgs& a, const LayerArgs* L, const typename FfnTraits<WF>::X* x, int nt,
+                       hipStream_t s) {
   if (L) {
-    if (a.act == ACT_REGLU) return launch_pred_up<W, ACT_REGLU, NT>(a, *L, x, nt, s);
-    if (a.act == ACT_RELU2) return launch_pred_up<W, ACT_RELU2, NT>(a, *L, x, nt, s);
-    return launch_pred_up<W, ACT_RELU, NT>(a, *L, x, nt, s);
+    if (a.act == ACT_REGLU) return launch_pred_up<WF, ACT_REGLU, NT>(a, *L, x, nt, s);
+    if (a.act == ACT_RELU2) return launch_pred_up<WF, ACT_RELU2, NT>(a, *L, x, nt, s);
+    return launch_pred_up<WF, ACT_RELU, NT>(a, *L, x, nt, s);
   }
-  if (a.act == ACT_REGLU) return launch_up<W, ACT_REGLU, NT>(a, x, nt, s);
-  if (a.act == ACT_RELU2) return launch_up<W, ACT_RELU2, NT>(a, x, nt, s);
-  return launch_up<W, ACT_RELU, NT>(a, x, nt, s);
+  if (a.act == ACT_REGLU) return launch_up<WF, ACT_REGLU, NT>(a, x, nt, s);
+  if (a.act == ACT_RELU2) return launch_up<WF, ACT_RELU2, NT>(a, x, nt, s);
+  return launch_up<WF, ACT_RELU, NT>(a, x, nt, s);
 }
 
-template <typename W, int NT>
+template <typename WF, int NT>
 hipError_t run_tile(const SparseArgs& a, const LayerArgs* L, int t0, int nt, hipStream_t s) {
-  const W* x = static_cast<const W*>(a.x) + (size_t)t0 * a.d;
-  hipError_t e = up_dispatch<W, NT>(a, L, x, nt, s);
+  using X = typename FfnTraits<WF>::X;
+  const X* x = static_cast<const X*>(a.x) + (size_t)t0 * a.d;
+  LayerArgs Lt;
+  if (L) {
+    Lt = *L;
+    Lt.t = L->t + (size_t)t0 * L->rank;
+  }
+  hipError_t e = up_dispatch<WF, NT>(a, L ? &Lt : nullptr, x, nt, s);
   if (e != hipSuccess) return e;
   const size_t yoff = (size_t)t0 * a.d * (a.ytype == 1 ? 2 : 4);
-  return launch_down<W, NT>(a, static_cast<char*>(a.y) + yoff, nt, s);
+  return launch_down<WF, NT>(a, static_cast<char*>(a.y) + yoff, nt, s);
 }
 
-template <typename W>
+template <typename WF>
 hipError_t run_all(const SparseArgs& a, const LayerArgs* L, hipStream_t s) {
-  const int tile = kSparseTile;
+  const int tile = sparse_tile(a.wtype, a.d);
   for (int t0 = 0; t0 < a.n_tok; t0 += tile) {
     const int nt = a.n_tok - t0 < tile ? a.n_tok - t0 : tile;
     hipError_t e;
     if (nt == 1)
-      e = run_tile<W, 1>(a, L, t0, nt, s);
+      e = run_tile<WF, 1>(a, L, t0, nt, s);
     else if (nt == 2)
-      e = run_tile<W, 2>(a, L, t0, nt, s);
+      e = run_tile<WF, 2>(a, L, t0, nt, s);
     else if (nt <= 4)
-      e = run_tile<W, 4>(a, L, t0, nt, s);
+      e = run_tile<WF, 4>(a, L, t0, nt, s);
     else
-      e = run_tile<W, 8>(a, L, t0, nt, s);
+      e = run_tile<WF, 8>(a, L, t0, nt, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+template <typename... Args>
+hipError_t by_wtype(int wtype, const SparseArgs& a, const LayerArgs* L, hipStream_t s) {
+  if (wtype == 1) return run_all<f16>(a, L, s);
+  if (wtype == 2) return run_all<Q4>(a, L, s);
+  return run_all<float>(a, L, s);
+}
+
 }  // namespace
 
+int sparse_tile(int wtype, int d) {
+  // Q4_0 keeps its fp16 activations in LDS: a tile of x must fit in 32 KB.
+  if (wtype != 2) return kSparseTile;
+  int tile = kSparseTile;
+  while (tile > 1 && (size_t)tile * d * 2 > 32768) tile >>= 1;
+  return tile;
+}
+
 void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices) {
-  const int E = wtype == 1 ? 8 : 4;
-  const int slices = (d + kWave * E - 1) / (kWave * E);
+  const int sw = wtype == 2 ? kDqSW : (wtype == 1 ? kWave * 8 : kWave * 4);
+  const int slices = (d + sw - 1) / sw;
   // Aim for about 2048 waves (8 per CU) in the down kernel.
   int c = (2048 / kDnWaves + slices - 1) / slices;
   if (c < 1) c = 1;
@@ -551,15 +812,11 @@ void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices) {
 
 int layer_segments(int d_ff) { return (d_ff + kPURows - 1) / kPURows; }
 
-hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s) {
-  if (a.wtype == 1) return run_all<f16>(a, nullptr, s);
-  return run_all<float>(a, nullptr, s);
-}
+hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s) { return by_wtype(a.wtype, a, nullptr, s); }
 
 hipError_t launch_layer_fused(const SparseArgs& a, const LayerArgs& L, hipStream_t s) {
-  // a single token tile: the caller guarantees n_tok <= kSparseTile
-  if (a.wtype == 1) return run_all<f16>(a, &L, s);
-  return run_all<float>(a, &L, s);
+  // a single token tile: the caller guarantees n_tok <= sparse_tile(wtype, d)
+  return by_wtype(a.wtype, a, &L, s);
 }
 
 }  // namespace pi

@@ -15,6 +15,13 @@ typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Tag type for Q4_0 FFN weights (repacked layout, see k_q4.hip); the
+// activations that multiply them are fp16.
+struct Q4 {};
+template <typename WF> struct FfnTraits { using X = WF; };
+template <> struct FfnTraits<Q4> { using X = f16; };
 
 constexpr int kWave = 64;
 
@@ -97,8 +104,9 @@ hipError_t launch_compact(const uint8_t* mask, int n_tok, int d_ff, int32_t* idx
                           hipStream_t s);
 
 // Sparse FFN (one call = all launches for n_tok tokens, in tiles of
-// kSparseTile tokens).
+// sparse_tile(wtype, d) <= kSparseTile tokens).
 constexpr int kSparseTile = 8;
+int sparse_tile(int wtype, int d);
 
 struct SparseArgs {
   int wtype, act, d, d_ff, n_tok, max_count;
@@ -112,8 +120,8 @@ struct SparseArgs {
   const int32_t* count;     // device count of valid list entries
   void* y;
   int ytype;
-  float* h;                 // workspace [kSparseTile][d_ff] fp32, by neuron number
-  float* part;              // workspace [n_chunks][kSparseTile][d] fp32
+  float* h;                 // workspace [tile][d_ff] fp32, by list position
+  float* part;              // workspace [n_chunks][tile][d] fp32
   int n_chunks, n_slices;
 };
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
@@ -131,7 +139,7 @@ struct LayerArgs {
   int32_t* idx;             // workspace [d_ff]
   int32_t* count;           // workspace, one int
 };
-// n_tok <= min(kSparseTile, pred_tile(rank)); a.idx / a.count must be L.idx / L.count.
+// n_tok <= min(sparse_tile(wtype, d), pred_tile(rank)); a.idx / a.count must be L.idx / L.count.
 hipError_t launch_layer_fused(const SparseArgs& a, const LayerArgs& L, hipStream_t s);
 // Number of neuron segments (workgroups) of the fused kernel.
 int layer_segments(int d_ff);

@@ -132,7 +132,10 @@ pi_status pi_compact(const uint8_t* mask, int32_t n_tok, int32_t d_ff,
 /* FFN over listed neurons only; unlisted neurons contribute exactly zero.
  *   x:         [n_tok][d_model]; xtype == ffn->wtype, or PI_F16 for Q4_0
  *   idx:       device int32 list, strictly increasing, values in [0, d_ff)
- *              (as pi_compact writes it); duplicates are undefined
+ *              (as pi_compact writes it); duplicates are undefined.  The
+ *              buffer must hold max_count entries: entries past *count may
+ *              be read (and ignored).  An entry outside [0, d_ff) adds
+ *              nothing.
  *   count:     device int32: number of valid entries of idx
  *   max_count: host bound on *count, in [0, d_ff]; sizes the launch (pass
  *              d_ff when unknown).  A device count above max_count is clamped
@@ -158,7 +161,10 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
  *        16 bytes; byte j holds code j in its low nibble and code j+16 in its
  *        high nibble; code q means weight d*(q-8))
  *   dst: rows*cols/32*18 bytes: all rows' 16-byte code groups first
- *        ([rows][cols/32][16]), then all scales ([rows][cols/32] fp16)
+ *        ([rows][cols/32][16]), then all scales ([rows][cols/32] fp16).
+ *        Inside a code group, 32-bit word k (k = 0..3, little-endian) holds
+ *        weight pairs p = 4k+u (u = 0..3): code 2p in bits [4u, 4u+4) and
+ *        code 2p+1 in bits [16+4u, 20+4u).
  * cols must be a multiple of 32.  src and dst must not overlap.
  * Cited passage: [GN] "Lượng tử hóa và tương thích" (INT4 Q4_0).  */
 pi_status pi_q4_0_repack(const void* src, int32_t rows, int32_t cols, void* dst, void* stream);
