@@ -80,8 +80,16 @@ Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
     const int tile = pi::sparse_tile(ffn->wtype, ffn->d_model);
     const int nt = n_tok < tile ? n_tok : tile;
     pi::sparse_chunking(ffn->wtype, ffn->d_model, &L.n_chunks, &L.n_slices);
-    L.h = take((size_t)nt * ffn->d_ff * sizeof(float));
-    L.part = take((size_t)L.n_chunks * nt * ffn->d_model * sizeof(float));
+    size_t hb = (size_t)nt * ffn->d_ff * sizeof(float);
+    size_t pb = (size_t)L.n_chunks * nt * ffn->d_model * sizeof(float);
+    if (pi::mfma_path(ffn->wtype, ffn->d_model, n_tok)) {
+      size_t mh, mp;
+      pi::mfma_workspace(ffn->wtype, ffn->d_model, ffn->d_ff, n_tok, &mh, &mp);
+      hb = hb > mh ? hb : mh;
+      pb = pb > mp ? pb : mp;
+    }
+    L.h = take(hb);
+    L.part = take(pb);
   }
   L.total = off;
   return L;

@@ -684,10 +684,7 @@ hipError_t launch_down(const SparseArgs& a, void* y, int nt, hipStream_t s) {
                        a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n = nt * a.d;
-  hipLaunchKernelGGL(k_merge, dim3((n + kMgThreads - 1) / kMgThreads), dim3(kMgThreads), 0, s, a.part, a.n_chunks,
-                     n, y, a.ytype);
-  return hipGetLastError();
+  return launch_merge(a.part, a.n_chunks, nt * a.d, y, a.ytype, s);
 }
 
 // x is staged in LDS when its token tile fits in 32 KB.
@@ -812,7 +809,17 @@ void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices) {
 
 int layer_segments(int d_ff) { return (d_ff + kPURows - 1) / kPURows; }
 
-hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s) { return by_wtype(a.wtype, a, nullptr, s); }
+hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_merge, dim3((n + kMgThreads - 1) / kMgThreads), dim3(kMgThreads), 0, s, part, n_chunks, n, y,
+                     ytype);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s) {
+  if (mfma_path(a.wtype, a.d, a.n_tok)) return launch_sparse_ffn_mfma(a, s);
+  return by_wtype(a.wtype, a, nullptr, s);
+}
 
 hipError_t launch_layer_fused(const SparseArgs& a, const LayerArgs& L, hipStream_t s) {
   // a single token tile: the caller guarantees n_tok <= sparse_tile(wtype, d)

@@ -148,6 +148,18 @@ int layer_segments(int d_ff);
 // columns (n_slices slices); sizes the workspace.
 void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices);
 
+// Multi-token path on the matrix cores (fp16 / Q4_0 weights, d % 128 == 0,
+// more tokens than one pass of the list path takes): used by
+// launch_sparse_ffn when mfma_path() says so.  Workspace: H [16*ceil(nt/16)]
+// [d_ff rounded up to 64] fp16 in a.h, partials [chunks][nt][d] fp32 in a.part
+// (nt = min(n_tok, 64)).
+bool mfma_path(int wtype, int d, int n_tok);
+void mfma_workspace(int wtype, int d, int d_ff, int n_tok, size_t* h_bytes, size_t* part_bytes);
+hipError_t launch_sparse_ffn_mfma(const SparseArgs& a, hipStream_t s);
+
+// y = sum over c of part[c][0 .. n), in chunk order (fp32 or fp16 out).
+hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, hipStream_t s);
+
 hipError_t launch_q4_0_repack(const void* src, int rows, int cols, void* dst, hipStream_t s);
 
 }  // namespace pi

@@ -141,19 +141,26 @@ def main(argv=None):
         return 1
     pi.load_library()
     cfg = workload.get_config(args.workload)
-    if cfg.wtype == "q4_0":
-        print("bench.py: Q4_0 workloads are not wired into the benchmark yet", file=sys.stderr)
-        return 2
     dev = torch.device("cuda")
     L, d, f = cfg.n_layers, cfg.d_model, cfg.d_ff
     T = args.warmup + args.steps
     xdt = torch.float16 if cfg.x_dtype == "f16" else torch.float32
 
+    n_base_layers, n_base_tok = 4, 16
+    q4 = cfg.wtype == "q4_0"
+    mats = ("w_up", "w_down_t", "w_gate")
     t_gen = time.perf_counter()
-    layers = []
+    layers, canon = [], []
     for li in range(L):
         lw = workload.make_layer(cfg, li, dev, args.seed)
         lw.pop("p")
+        if q4:
+            # the kernels read the repacked layout; the oracle reads canonical blocks
+            if li < n_base_layers and not args.no_cpu_baseline:
+                canon.append({k: lw[k].cpu().numpy() for k in mats if k in lw})
+            for k in mats:
+                if k in lw:
+                    lw[k] = pi.q4_0_repack(lw[k], f, d)
         layers.append(lw)
         if (li + 1) % 10 == 0:
             print(f"[bench] generated layer {li + 1}/{L}", file=sys.stderr, flush=True)
@@ -165,7 +172,7 @@ def main(argv=None):
 
     preds = [pi.Predictor(lw["p1"], lw["p2"], lw["c"]) for lw in layers]
     ffns = [pi.FFN(lw["w_up"], lw["w_down_t"], cfg.act, b_up=lw.get("b_up"), w_gate=lw.get("w_gate"),
-                   b_gate=lw.get("b_gate")) for lw in layers]
+                   b_gate=lw.get("b_gate"), d_model=d if q4 else None) for lw in layers]
     ws_bytes = pi.workspace_bytes(preds[0], ffns[0], 1)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     x_stage = torch.zeros((L, d), dtype=xdt, device=dev)
@@ -255,12 +262,13 @@ def main(argv=None):
     # whole-layer bytes per layer-token, averaged over the timed steps
     b_layer = float(np.mean([bytes_layer(cfg, c) for c in counts.flat]))
     ms_layer = ms_step / L
-    layer_roof = roof("pi_layer (k_pred1 + k_pred_up + k_down + k_merge)", b_layer, ms_layer)
+    dn = "k_down_q4" if q4 else "k_down"
+    layer_roof = roof(f"pi_layer (k_pred1 + k_pred_up + {dn} + k_merge)", b_layer, ms_layer)
     parts = {
         "predict": roof("pi_predict (k_pred1 + k_pred2)", b_pred, ms_pred),
         "compact": {"kernel": "pi_compact (k_compact)", "avg_launch_us": round(ms_comp * 1e3, 3),
                     "bytes_per_launch": int(b_comp)},
-        "gather": roof("pi_sparse_ffn (k_up + k_down + k_merge)", b_sp, ms_sp),
+        "gather": roof(f"pi_sparse_ffn (k_up + {dn} + k_merge)", b_sp, ms_sp),
     }
     parts["gather"]["active_weight_gbps"] = round(b_act / (ms_sp * 1e-3) / 1e9, 1)
     parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
@@ -290,17 +298,21 @@ def main(argv=None):
     }
 
     if not args.no_cpu_baseline:
-        import oracle  # noqa: F401  (the baseline leg is the only user of the oracle here)
-        n_base_layers, n_base_tok = 4, 16
+        import oracle  # the baseline leg is the only user of the oracle here
         host_layers = []
         for li in range(n_base_layers):
             lw = layers[li]
+
+            def w(k):
+                if k not in lw:
+                    return None
+                return oracle.Q4_0Matrix(canon[li][k], d) if q4 else lw[k].cpu().numpy()
+
             host_layers.append({
                 "p1": lw["p1"].cpu().numpy(), "p2": lw["p2"].cpu().numpy(), "c": lw["c"].cpu().numpy(),
-                "ffn": {"w_up": lw["w_up"].cpu().numpy(), "w_down_t": lw["w_down_t"].cpu().numpy(),
-                        "act": cfg.act,
+                "ffn": {"w_up": w("w_up"), "w_down_t": w("w_down_t"), "act": cfg.act,
                         "b_up": lw["b_up"].cpu().numpy() if "b_up" in lw else None,
-                        "w_gate": lw["w_gate"].cpu().numpy() if "w_gate" in lw else None,
+                        "w_gate": w("w_gate"),
                         "b_gate": lw["b_gate"].cpu().numpy() if "b_gate" in lw else None},
             })
         xs = x_all[args.warmup:args.warmup + n_base_tok, :n_base_layers].cpu().numpy()

@@ -130,6 +130,61 @@ def test_sparse_ffn(dtype, d, f, act, n_tok):
                 check_y(host(y), ref, tol, f"{act} d={d} f={f} n={n_tok}")
 
 
+# Multi-token path (matrix cores): more tokens than one list-path pass.
+MFMA_SHAPES = [
+    (128, 300),      # one 128-wide k step: three of the four k-split waves have no work
+    (1024, 1000),    # ragged list tail (count not a multiple of 32 or 64)
+    (8192, 700),     # model width
+]
+
+
+@pytest.mark.parametrize("d,f", MFMA_SHAPES)
+@pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
+@pytest.mark.parametrize("n_tok", [9, 16, 17, 40, 64, 65, 130])
+def test_sparse_ffn_mfma(d, f, act, n_tok):
+    dtype = torch.float16
+    kw = rand_ffn(d, f, act, dtype, seed=d + f + n_tok + 1)
+    ffn = pi.FFN(**kw)
+    hk = host_ffn(kw)
+    g = torch.Generator(device="cuda").manual_seed(3 * n_tok + f)
+    x = torch.randn((n_tok, d), generator=g, device="cuda").to(dtype)
+    for density in (0.05, 0.5, 1.0):
+        sel = torch.rand(f, generator=g, device="cuda") < density
+        idx_list = torch.nonzero(sel).flatten().to(torch.int32)
+        n = idx_list.numel()
+        idx = torch.full((f,), -3, dtype=torch.int32, device="cuda")      # entries past the count are junk
+        idx[:n] = idx_list
+        cnt = torch.tensor([n], dtype=torch.int32, device="cuda")
+        y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+        pi.sparse_ffn(ffn, x, idx, cnt, y)
+        ref = oracle.sparse_ffn(host(x), host(idx_list), **hk)
+        check_y(host(y), ref, TOL["f16"], f"mfma {act} d={d} f={f} n={n_tok} density={density}")
+
+
+def test_mfma_empty_clamped_deterministic():
+    d, f, n_tok = 1024, 800, 24
+    kw = rand_ffn(d, f, "reglu", torch.float16, seed=5)
+    ffn, hk = pi.FFN(**kw), host_ffn(kw)
+    x = torch.randn((n_tok, d), device="cuda").to(torch.float16)
+    s = np.flatnonzero(np.random.default_rng(2).random(f) < 0.4).astype(np.int32)
+    idx = _i32(f)
+    idx[:len(s)] = torch.as_tensor(s, device="cuda")
+
+    def run(count, max_count=None, ytype=torch.float32):
+        cnt = torch.tensor([count], dtype=torch.int32, device="cuda")
+        y = torch.full((n_tok, d), float("nan"), dtype=ytype, device="cuda")
+        pi.sparse_ffn(ffn, x, idx, cnt, y, max_count=max_count)
+        return y
+
+    assert torch.all(run(0) == 0)                                       # empty list: exact zeros
+    check_y(host(run(len(s), max_count=37)), oracle.sparse_ffn(host(x), s[:37], **hk), TOL["f16"], "clamped")
+    y1, y2 = run(len(s)), run(len(s))
+    assert torch.equal(y1, y2)                                          # bitwise reproducible
+    y16 = run(len(s), ytype=torch.float16)
+    ref = oracle.sparse_ffn(host(x), s, **hk)
+    check_y(host(y16), ref.astype(np.float16).astype(np.float64), TOL["f16"] + 1e-3, "fp16 out")
+
+
 @pytest.mark.parametrize("act", ["relu", "reglu"])
 def test_superset_all_empty_partition(act):
     dtype, d, f, n_tok = torch.float16, 1024, 2048, 2

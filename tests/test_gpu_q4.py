@@ -109,6 +109,27 @@ def test_sparse_ffn_q4(d, f, act, n_tok):
         check_y(host(y), ref, TOL["q4_0"], f"q4 {act} d={d} f={f} n={n_tok} density={density}")
 
 
+@pytest.mark.parametrize("d,f", [(1024, 900), (8192, 500)])
+@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("n_tok", [3, 8, 9, 16, 33, 64])
+def test_sparse_ffn_q4_mfma(d, f, act, n_tok):
+    # More tokens than one list-path pass: the matrix-core path.
+    ffn, hk, _ = _q4_ffn(d, f, act, seed=d + 7 * f + n_tok)
+    g = torch.Generator(device="cuda").manual_seed(11 * n_tok + f)
+    x = torch.randn((n_tok, d), generator=g, device="cuda").to(torch.float16)
+    for density in (0.05, 0.4):
+        sel = torch.rand(f, generator=g, device="cuda") < density
+        idx_list = torch.nonzero(sel).flatten().to(torch.int32)
+        n = idx_list.numel()
+        idx = _i32(f)
+        idx[:n] = idx_list
+        cnt = torch.tensor([n], dtype=torch.int32, device="cuda")
+        y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+        pi.sparse_ffn(ffn, x, idx, cnt, y)
+        ref = oracle.sparse_ffn(host(x), host(idx_list), **hk)
+        check_y(host(y), ref, TOL["q4_0"], f"q4 mfma {act} d={d} f={f} n={n_tok} density={density}")
+
+
 def test_q4_empty_and_all():
     d, f, n_tok = 1024, 512, 3
     ffn, hk, _ = _q4_ffn(d, f, "reglu", seed=11)
