@@ -55,7 +55,7 @@ int x_type_of(const pi_ffn* f) { return f->wtype == PI_Q4_0 ? PI_F16 : f->wtype;
 // Workspace: each entry point lays out only the sections it uses, in this
 // order, every section 256-byte aligned.
 struct Layout {
-  size_t t = 0, mask = 0, idx = 0, count = 0, status = 0, h = 0, part = 0;
+  size_t t = 0, tpart = 0, mask = 0, idx = 0, count = 0, status = 0, h = 0, part = 0;
   size_t total = 0;
   int n_chunks = 0, n_slices = 0, n_segments = 0;
 };
@@ -68,7 +68,11 @@ Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
     off += up256(bytes);
     return o;
   };
-  if (pred) L.t = take((size_t)n_tok * pred->rank * sizeof(float));
+  if (pred) {
+    L.t = take((size_t)n_tok * pred->rank * sizeof(float));
+    if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok))
+      L.tpart = take(pi::pred_mfma_part_bytes(pred->d_model, pred->rank, n_tok));
+  }
   if (pred && ffn) {
     L.mask = take((size_t)n_tok * ffn->d_ff);
     L.idx = take((size_t)ffn->d_ff * sizeof(int32_t));
@@ -113,6 +117,20 @@ float theta_of(float tau) {
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Masks (and optional logits) of n_tok tokens: the matrix-core predictor for
+// many fp16 tokens, else the two predictor stages.
+hipError_t predict_any(const pi_predictor* pred, const void* x, int n_tok, float theta, float* t, char* ws,
+                       const Layout& L, uint8_t* mask, float* logits, hipStream_t s) {
+  if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok))
+    return pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
+                                   theta, t, ws + L.tpart, mask, logits, s);
+  hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, nullptr,
+                                           0, s);
+  if (e != hipSuccess) return e;
+  return pi::launch_predict_stage2(pred->wtype, pred->p2, pred->c, t, n_tok, pred->rank, pred->d_ff, theta, mask,
+                                   logits, s);
+}
 
 pi::SparseArgs sparse_args(const pi_ffn* f, const void* x, int n_tok, const int32_t* idx, const int32_t* count,
                            int max_count, void* y, int ytype, char* ws, const Layout& L) {
@@ -164,11 +182,8 @@ pi_status pi_predict(const pi_predictor* pred, const void* x, int32_t xtype, int
   const Layout L = layout(pred, nullptr, n_tok);
   if ((st = check_ws(ws, ws_bytes, L.total)) != PI_OK) return st;
   float* t = reinterpret_cast<float*>(static_cast<char*>(ws) + L.t);
-  hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t,
-                                           nullptr, 0, as_stream(stream));
-  if (e != hipSuccess) return hip_fail(e);
-  e = pi::launch_predict_stage2(pred->wtype, pred->p2, pred->c, t, n_tok, pred->rank, pred->d_ff, theta_of(tau),
-                                mask, logits, as_stream(stream));
+  const hipError_t e = predict_any(pred, x, n_tok, theta_of(tau), t, static_cast<char*>(ws), L, mask, logits,
+                                   as_stream(stream));
   if (e != hipSuccess) return hip_fail(e);
   return PI_OK;
 }
@@ -226,12 +241,14 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
   unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   const hipStream_t s = as_stream(stream);
   pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
-  const bool fused = n_tok <= pi::sparse_tile(ffn->wtype, ffn->d_model) && n_tok <= pi::pred_tile(pred->rank);
-  // Stage 1 also clears the fused kernel's segment counters.
-  hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t,
-                                           fused ? status : nullptr, fused ? L.n_segments : 0, s);
-  if (e != hipSuccess) return hip_fail(e);
+  const bool fused = n_tok <= pi::sparse_tile(ffn->wtype, ffn->d_model) && n_tok <= pi::pred_tile(pred->rank) &&
+                     !pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok);
+  hipError_t e;
   if (fused) {
+    // Stage 1 also clears the fused kernel's segment counters.
+    e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, status,
+                                  L.n_segments, s);
+    if (e != hipSuccess) return hip_fail(e);
     pi::LayerArgs la;
     la.p2 = pred->p2;
     la.c = pred->c;
@@ -246,8 +263,7 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
     return PI_OK;
   }
   // Many tokens: predict every token, take the union list, then the list path.
-  e = pi::launch_predict_stage2(pred->wtype, pred->p2, pred->c, t, n_tok, pred->rank, pred->d_ff, theta_of(tau),
-                                mask, nullptr, s);
+  e = predict_any(pred, x, n_tok, theta_of(tau), t, w, L, mask, nullptr, s);
   if (e != hipSuccess) return hip_fail(e);
   e = pi::launch_compact(mask, n_tok, ffn->d_ff, idx, count, s);
   if (e != hipSuccess) return hip_fail(e);

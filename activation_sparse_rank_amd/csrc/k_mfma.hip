@@ -92,6 +92,33 @@ __device__ __forceinline__ int clamp_count(const int32_t* count_ptr, int max_cou
   return c < 0 ? 0 : (c < max_count ? c : max_count);
 }
 
+// The 4 waves of a workgroup hold accumulators for the same NQ output quads
+// (16x16 blocks, 4 values per lane); sum them in wave order through LDS
+// (red: [4][NQ][4][64] floats).  Thread T gets lane position T%64 of quads
+// q = T/64 + 4e, e < NQ/4, in out[e][0..3].
+template <int NQ>
+__device__ __forceinline__ void sum_waves(float* red, const f32x4 (&acc)[NQ], float (&out)[NQ / 4][4]) {
+  const int lane = lane_id(), wave = wave_id();
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave * NQ + q) * 4 + i) * kWave + lane] = acc[q][i];
+  __syncthreads();
+  const int ol = threadIdx.x & (kWave - 1), oq = threadIdx.x >> 6;
+#pragma unroll
+  for (int e = 0; e < NQ / 4; ++e) {
+    const int q = oq + 4 * e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = red[((0 * NQ + q) * 4 + i) * kWave + ol];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) v += red[((w * NQ + q) * 4 + i) * kWave + ol];
+      out[e][i] = v;
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // k_mup
 // ---------------------------------------------------------------------------
@@ -101,23 +128,127 @@ constexpr int kMuMB = 4;                   // 16-row blocks per wave (all waves 
 constexpr int kMuRows = 16 * kMuMB;        // list positions per workgroup
 constexpr int kMuK = 128;                  // k per step: 4 lane groups x 32
 
-// The 4 A operands (k = k0 + 8s .. +8, s = 0..3) of one row for this lane.
+// Operands of one 128-wide k step [kb, kb + 128) for this lane (group g =
+// lane/16).  MFMA sub-step s (0..3) multiplies the A and B operands
+// a[s], b[s]; both must cover the same 32 k values, in any order.
+//
+// fp16 rows ("natural order"): sub-step s, group g -> k = kb + 32s + 8g + 0..7,
+// so one load instruction reads 64 contiguous bytes of each of 16 rows.
+__device__ __forceinline__ void ld_k128(const f16* rowkb, bool ok, int g, bool stream, u32x4 (&a)[4]) {
+  const char* p = reinterpret_cast<const char*>(rowkb + 8 * g);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    a[s] = ok ? (stream ? ld_nt(p + 64 * s) : ld16(p + 64 * s)) : u32x4{0, 0, 0, 0};
+}
+
+// Q4_0 rows ("block order"): group g owns block kb/32 + g (one 16-byte code
+// group and one scale); sub-step s takes its word s -> k = kb + 32g + 8s + 0..7.
+// The fp16 operand that meets it must be permuted to match (k_xstep).
+__device__ __forceinline__ void ld_k128_q4(const uint8_t* w, size_t scale_off, int row, bool ok, int d, int kb,
+                                           int g, u32x4 (&a)[4]) {
+  const size_t blk = (size_t)row * (d / 32) + kb / 32 + g;
+  const u32x4 code = ok ? ld_nt(w + blk * 16) : u32x4{0, 0, 0, 0};
+  const f16 sc = ok ? reinterpret_cast<const f16*>(w + scale_off)[blk] : (f16)0.0f;
+  const f16x2 s2{sc, sc};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a[s] = q4_dequant8(dw(code, s), s2);
+}
+
 template <typename WF>
-__device__ __forceinline__ void load_row_k32(const void* w, size_t scale_off, int row, bool ok, int d, int k0,
-                                             u32x4 (&a)[4]) {
-  if constexpr (std::is_same<WF, Q4>::value) {
-    const int nbk = d / 32;
-    const size_t blk = (size_t)row * nbk + k0 / 32;
-    const u32x4 code = ok ? ld_nt(static_cast<const uint8_t*>(w) + blk * 16) : u32x4{0, 0, 0, 0};
-    const f16 sc = ok ? reinterpret_cast<const f16*>(static_cast<const uint8_t*>(w) + scale_off)[blk] : (f16)0.0f;
-    const f16x2 s2{sc, sc};
+__device__ __forceinline__ void load_row_k128(const void* w, size_t scale_off, int row, bool ok, int d, int kb, int g,
+                                              u32x4 (&a)[4]) {
+  if constexpr (std::is_same<WF, Q4>::value)
+    ld_k128_q4(static_cast<const uint8_t*>(w), scale_off, row, ok, d, kb, g, a);
+  else
+    ld_k128(static_cast<const f16*>(w) + (size_t)row * d + kb, ok, g, true, a);
+}
+
+// One 128-wide k step of MB 16-row blocks of a weight matrix, held as loaded
+// (fp16: the operands themselves; Q4_0: the code groups and scales, turned
+// into fp16 operands when used), so that the next step's loads can be in
+// flight while this one is multiplied.
+template <typename WF, int MB>
+struct RowStep {
+  u32x4 v[MB][4];
+  __device__ __forceinline__ void load(const void* w, size_t, const int (&row)[MB], const bool (&rv)[MB], int d,
+                                       int kb, int g) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = q4_dequant8(dw(code, s), s2);
-  } else {
-    const char* p = static_cast<const char*>(w) + ((size_t)row * d + k0) * sizeof(f16);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = ok ? ld_nt(p + 16 * s) : u32x4{0, 0, 0, 0};
+    for (int mb = 0; mb < MB; ++mb) ld_k128(static_cast<const f16*>(w) + (size_t)row[mb] * d + kb, rv[mb], g, true, v[mb]);
   }
+  __device__ __forceinline__ void operands(int mb, u32x4 (&a)[4]) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = v[mb][s];
+  }
+};
+
+template <int MB>
+struct RowStep<Q4, MB> {
+  u32x4 code[MB];
+  f16 sc[MB];
+  __device__ __forceinline__ void load(const void* w, size_t scale_off, const int (&row)[MB], const bool (&rv)[MB],
+                                       int d, int kb, int g) {
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const size_t blk = (size_t)row[mb] * (d / 32) + kb / 32 + g;
+      code[mb] = rv[mb] ? ld_nt(wb + blk * 16) : u32x4{0, 0, 0, 0};
+      sc[mb] = rv[mb] ? reinterpret_cast<const f16*>(wb + scale_off)[blk] : (f16)0.0f;
+    }
+  }
+  __device__ __forceinline__ void operands(int mb, u32x4 (&a)[4]) const {
+    const f16x2 s2{sc[mb], sc[mb]};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = q4_dequant8(dw(code[mb], s), s2);
+  }
+};
+
+// NB 16-token blocks of fp16 activations for step st, from a step-major
+// copy xs[step][token][128] (see k_xstep): one step's operands of all tokens
+// are one contiguous block, so the many workgroups reading them at once
+// spread over the L2 channels instead of meeting on the few that a 16 KB row
+// stride maps to.
+template <int NB>
+struct TokStep {
+  u32x4 v[NB][4];
+  __device__ __forceinline__ void load(const f16* xs, int nt, int st, int g, int n16) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int t = nb * 16 + n16;
+      ld_k128(xs + ((size_t)st * nt + t) * kMuK, t < nt, g, false, v[nb]);
+    }
+  }
+};
+
+// Run steps [s0, s1) with two register stages: the loads of step st+1 are
+// issued before step st is multiplied.  load(stage, st) and mul(stage) are
+// the caller's.
+template <typename Stage, typename Load, typename Mul>
+__device__ __forceinline__ void pipeline2(int s0, int s1, Stage& A, Stage& B, Load load, Mul mul) {
+  if (s0 >= s1) return;
+  load(A, s0);
+  for (int st = s0; st < s1; st += 2) {
+    if (st + 1 < s1) load(B, st + 1);
+    mul(A);
+    if (st + 2 < s1) load(A, st + 2);
+    if (st + 1 < s1) mul(B);
+  }
+}
+
+// k_xstep: xs[st][t][128] = x[t][128 st .. 128 st + 128), the step-major copy
+// TokStep reads.  With BLOCK (operands meeting Q4_0 rows, which come in block
+// order) the 16-byte groups inside a step are also permuted:
+// xs[st][t][32s + 8g + j] = x[t][128 st + 32g + 8s + j].  One thread per
+// 16-byte group.
+template <bool BLOCK>
+__global__ __launch_bounds__(256) void k_xstep(const f16* __restrict__ x, int nt, int d, f16* __restrict__ xs) {
+  const int e = blockIdx.x * 256 + threadIdx.x;       // destination group: [st][t][s][g]
+  const int groups = nt * d / 8;
+  if (e >= groups) return;
+  const int q = e & 15, rest = e >> 4;
+  const int t = rest % nt, st = rest / nt;
+  const int src_q = BLOCK ? ((q & 3) << 2) | (q >> 2) : q;
+  *reinterpret_cast<u32x4*>(xs + (size_t)e * 8) =
+      *reinterpret_cast<const u32x4*>(x + (size_t)t * d + st * kMuK + src_q * 8);
 }
 
 template <typename WF, int ACT, int NB>
@@ -158,30 +289,44 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
 
   const int ns = d / kMuK;
   const int s0 = wave * ns / kMuWaves, s1 = (wave + 1) * ns / kMuWaves;
-  for (int st = s0; st < s1; ++st) {
-    const int k0 = st * kMuK + g * 32;
-    u32x4 a[kMuMB][4], ga[GATED ? kMuMB : 1][4], b[NB][4];
+  struct Step {
+    RowStep<WF, kMuMB> up;
+    RowStep<WF, GATED ? kMuMB : 1> gate;
+    TokStep<NB> x;
+  };
+  auto load = [&](Step& S, int st) {
+    const int kb = st * kMuK;
+    S.up.load(w_up, scale_off, row, rv, d, kb, g);
+    if constexpr (GATED) S.gate.load(w_gate, scale_off, row, rv, d, kb, g);
+    S.x.load(x, nt, st, g, n16);
+  };
+  auto mul = [&](const Step& S) {
 #pragma unroll
     for (int mb = 0; mb < kMuMB; ++mb) {
-      load_row_k32<WF>(w_up, scale_off, row[mb], rv[mb], d, k0, a[mb]);
-      if (GATED) load_row_k32<WF>(w_gate, scale_off, row[mb], rv[mb], d, k0, ga[mb]);
-    }
+      u32x4 a[4], ga[4];
+      S.up.operands(mb, a);
+      if constexpr (GATED) S.gate.operands(mb, ga);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int t = nb * 16 + n16;
-      const char* xp = reinterpret_cast<const char*>(x + (size_t)t * d + k0);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) b[nb][s] = t < nt ? ld16(xp + 16 * s) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int mb = 0; mb < kMuMB; ++mb)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          au[mb][nb] = mfma(a[mb][s], b[nb][s], au[mb][nb]);
-          if (GATED) ag[mb][nb] = mfma(ga[mb][s], b[nb][s], ag[mb][nb]);
+          au[mb][nb] = mfma(a[s], S.x.v[nb][s], au[mb][nb]);
+          if constexpr (GATED) ag[mb][nb] = mfma(ga[s], S.x.v[nb][s], ag[mb][nb]);
         }
+    }
+  };
+  // Two stages in flight unless their registers would crowd out the
+  // accumulators (measured: Q4_0 rows run faster with one stage).
+  constexpr bool kPipe = !(GATED && NB > 2) && !std::is_same<WF, Q4>::value;
+  if constexpr (kPipe) {
+    Step S0, S1;
+    pipeline2(s0, s1, S0, S1, load, mul);
+  } else {
+    for (int st = s0; st < s1; ++st) {
+      Step S;
+      load(S, st);
+      mul(S);
+    }
   }
 
   // Sum the 4 waves in wave order.  Thread T owns lane position T%64 and the
@@ -190,29 +335,17 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   const int ol = threadIdx.x & (kWave - 1);
   const int oq = threadIdx.x >> 6;
   float su[NB][4], sg[NB][4];
-  auto reduce = [&](f32x4 (&acc)[kMuMB][NB], float (&out)[NB][4]) {
+  {
+    f32x4 flat[NQ];
+    if constexpr (GATED) {
 #pragma unroll
-    for (int mb = 0; mb < kMuMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][mb * NB + nb][i][lane] = acc[mb][nb][i];
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < NB; ++e) {
-      const int q = oq + kMuWaves * e;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = red[0][q][i][ol];
-#pragma unroll
-        for (int w = 1; w < kMuWaves; ++w) v += red[w][q][i][ol];
-        out[e][i] = v;
-      }
+      for (int q = 0; q < NQ; ++q) flat[q] = ag[q / NB][q % NB];
+      sum_waves<NQ>(&red[0][0][0][0], flat, sg);
     }
-    __syncthreads();
-  };
-  if constexpr (GATED) reduce(ag, sg);
-  reduce(au, su);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) flat[q] = au[q / NB][q % NB];
+    sum_waves<NQ>(&red[0][0][0][0], flat, su);
+  }
 
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
@@ -391,6 +524,176 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
 }
 
 // ---------------------------------------------------------------------------
+// Predictor for many tokens ([QB] "Гибридный дизайн вывода CPU/GPU": the
+// predictor maps the input to the neurons expected to fire; two low-rank
+// products and a threshold).  Same tiling as k_mup, over all rows:
+//   k_mp1    -- part[s][j][r] = sum over k in split s of p1[r][k] * x[j][k]
+//               (the k range is split over the grid's y dimension, then over
+//               the 4 waves);
+//   k_tsplit -- t = the splits added in order (fp32), and t_hi = fp16(t),
+//               t_lo = fp16(t - t_hi);
+//   k_mp2    -- l[j][i] = p2[i] . t[j] + c[i]; mask = l > theta.  t is fp32,
+//               so both t_hi and t_lo are multiplied (products exact in fp32;
+//               t_hi + t_lo carries 22 significant bits).  Needs |t| < 65504.
+// ---------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, const f16* __restrict__ x, int d,
+                                                    int rank, int nt, float* __restrict__ part) {
+  // x: the step-major copy of the token tile (k_xstep)
+  constexpr int NQ = kMuMB * NB;
+  __shared__ float red[kMuWaves][NQ][4][kWave];
+  const int lane = lane_id(), wave = wave_id();
+  const int g = lane >> 4, n16 = lane & 15;
+  const int r0 = blockIdx.x * kMuRows;
+  const int split = blockIdx.y, n_split = gridDim.y;
+  int row[kMuMB];
+  bool rv[kMuMB];
+#pragma unroll
+  for (int mb = 0; mb < kMuMB; ++mb) {
+    row[mb] = r0 + mb * 16 + n16;
+    rv[mb] = row[mb] < rank;
+  }
+  f32x4 acc[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ns = d / kMuK;
+  const int c0 = split * ns / n_split, c1 = (split + 1) * ns / n_split;
+  const int s0 = c0 + wave * (c1 - c0) / kMuWaves, s1 = c0 + (wave + 1) * (c1 - c0) / kMuWaves;
+#pragma unroll
+  for (int mb = 0; mb < kMuMB; ++mb) row[mb] = rv[mb] ? row[mb] : 0;
+  struct Step {
+    RowStep<f16, kMuMB> w;
+    TokStep<NB> x;
+  };
+  auto load = [&](Step& S, int st) {
+    S.w.load(p1, 0, row, rv, d, st * kMuK, g);
+    S.x.load(x, nt, st, g, n16);
+  };
+  auto mul = [&](const Step& S) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mb = 0; mb < kMuMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.x.v[nb][s], acc[mb * NB + nb]);
+  };
+  Step S0, S1;
+  pipeline2(s0, s1, S0, S1, load, mul);
+  float sum[NB][4];
+  sum_waves<NQ>(&red[0][0][0][0], acc, sum);
+  const int ol = threadIdx.x & (kWave - 1), oq = threadIdx.x >> 6;
+#pragma unroll
+  for (int e = 0; e < NB; ++e) {
+    const int q = oq + 4 * e;
+    const int mb = q / NB, nb = q % NB;
+    const int j = nb * 16 + (ol & 15);
+    const int r = r0 + mb * 16 + 4 * (ol >> 4);     // rank % 8 == 0: r < rank means r + 3 < rank
+    if (j < nt && r < rank)
+      *reinterpret_cast<f32x4*>(part + ((size_t)split * nt + j) * rank + r) =
+          f32x4{sum[e][0], sum[e][1], sum[e][2], sum[e][3]};
+  }
+}
+
+// k_tsplit: t = sum of the k splits of the first product in split order
+// (fp32), and its fp16 split t_hi = fp16(t), t_lo = fp16(t - t_hi), stored
+// step-major ([rank/128][nt][128]) for k_mp2.
+__global__ __launch_bounds__(256) void k_tsplit(const float* __restrict__ part, int n_split, int nt, int rank,
+                                                float* __restrict__ t, f16* __restrict__ th, f16* __restrict__ tl) {
+  const int n = nt * rank;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float v[16];
+#pragma unroll
+  for (int sp = 0; sp < 16; ++sp) v[sp] = sp < n_split ? part[(size_t)sp * n + e] : 0.f;
+  float sum = v[0];
+#pragma unroll
+  for (int sp = 1; sp < 16; ++sp)
+    if (sp < n_split) sum += v[sp];
+  t[e] = sum;
+  const f16 hi = (f16)sum;
+  const int j = e / rank, r = e - j * rank;
+  const size_t o = ((size_t)(r / kMuK) * nt + j) * kMuK + r % kMuK;     // step-major, as TokStep reads
+  th[o] = hi;
+  tl[o] = (f16)(sum - (float)hi);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, const float* __restrict__ c,
+                                                    const f16* __restrict__ th, const f16* __restrict__ tl, int rank,
+                                                    int d_ff, int nt, float theta, uint8_t* __restrict__ mask,
+                                                    float* __restrict__ logits) {
+  constexpr int NQ = kMuMB * NB;
+  __shared__ float red[kMuWaves][NQ][4][kWave];
+  const int lane = lane_id(), wave = wave_id();
+  const int g = lane >> 4, n16 = lane & 15;
+  const int r0 = blockIdx.x * kMuRows;
+  int row[kMuMB];
+  bool rv[kMuMB];
+#pragma unroll
+  for (int mb = 0; mb < kMuMB; ++mb) {
+    row[mb] = r0 + mb * 16 + n16;
+    rv[mb] = row[mb] < d_ff;
+  }
+  f32x4 acc[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ns = rank / kMuK;
+  const int s0 = wave * ns / kMuWaves, s1 = (wave + 1) * ns / kMuWaves;
+#pragma unroll
+  for (int mb = 0; mb < kMuMB; ++mb) row[mb] = rv[mb] ? row[mb] : 0;
+  struct Step {
+    RowStep<f16, kMuMB> w;
+    TokStep<NB> hi, lo;
+  };
+  auto load = [&](Step& S, int st) {
+    S.w.load(p2, 0, row, rv, rank, st * kMuK, g);
+    S.hi.load(th, nt, st, g, n16);
+    S.lo.load(tl, nt, st, g, n16);
+  };
+  auto mul = [&](const Step& S) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mb = 0; mb < kMuMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.hi.v[nb][s], acc[mb * NB + nb]);
+          acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.lo.v[nb][s], acc[mb * NB + nb]);
+        }
+  };
+  if constexpr (NB <= 2) {
+    Step S0, S1;
+    pipeline2(s0, s1, S0, S1, load, mul);
+  } else {
+    for (int st = s0; st < s1; ++st) {
+      Step S;
+      load(S, st);
+      mul(S);
+    }
+  }
+  float sum[NB][4];
+  sum_waves<NQ>(&red[0][0][0][0], acc, sum);
+  const int ol = threadIdx.x & (kWave - 1), oq = threadIdx.x >> 6;
+#pragma unroll
+  for (int e = 0; e < NB; ++e) {
+    const int q = oq + 4 * e;
+    const int mb = q / NB, nb = q % NB;
+    const int j = nb * 16 + (ol & 15);
+    const int r = r0 + mb * 16 + 4 * (ol >> 4);
+    if (j < nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (r + i < d_ff) {
+          const float l = sum[e][i] + c[r + i];
+          mask[(size_t)j * d_ff + r + i] = l > theta ? 1 : 0;
+          if (logits) logits[(size_t)j * d_ff + r + i] = l;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 constexpr int kMfmaTile = 64;              // tokens per pass
@@ -402,7 +705,20 @@ constexpr int down_cpl(int nb) {
 
 int mfma_chunks(int wtype) { return wtype == 2 ? 16 : 8; }
 
+// k splits of the predictor's first product: about 4 steps of 128 per split.
+int pred_splits(int d) {
+  const int ns = d / kMuK;
+  int sp = ns / 4;
+  return sp < 1 ? 1 : (sp > 16 ? 16 : sp);
+}
+
 int ldh_of(int d_ff) { return (d_ff + kMuRows - 1) / kMuRows * kMuRows; }
+
+size_t up256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Sparse FFN workspace of one token tile: H [64][ldh] fp16, then the
+// step-major activations [d/128][nt][128] fp16.
+size_t h_region(int d_ff, int nb) { return up256((size_t)16 * nb * ldh_of(d_ff) * sizeof(f16)); }
 
 template <typename WF, int ACT, int NB>
 hipError_t launch_mup(const SparseArgs& a, const f16* x, int nt, f16* h, int ldh, hipStream_t s) {
@@ -421,6 +737,15 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
   f16* h = reinterpret_cast<f16*>(a.h);
   const int ldh = ldh_of(a.d_ff);
   hipError_t e;
+  {
+    f16* xs = reinterpret_cast<f16*>(reinterpret_cast<char*>(a.h) + h_region(a.d_ff, 4));
+    const int n_groups = nt * a.d / 8;
+    hipLaunchKernelGGL((k_xstep<std::is_same<WF, Q4>::value>), dim3((n_groups + 255) / 256), dim3(256), 0, s, x, nt,
+                       a.d, xs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    x = xs;
+  }
   if (a.act == ACT_REGLU)
     e = launch_mup<WF, ACT_REGLU, NB>(a, x, nt, h, ldh, s);
   else if (a.act == ACT_RELU2)
@@ -458,6 +783,34 @@ hipError_t run_mall(const SparseArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+// Workspace of one predictor token tile: the k-split partials, t_hi, t_lo
+// and the step-major copy of the tokens.
+
+template <int NB>
+hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x, int nt, int d, int rank, int d_ff,
+                     float theta, float* t, char* ws, uint8_t* mask, float* logits, hipStream_t s) {
+  const int splits = pred_splits(d);
+  float* part = reinterpret_cast<float*>(ws);
+  f16* th = reinterpret_cast<f16*>(ws + up256((size_t)splits * kMfmaTile * rank * sizeof(float)));
+  f16* tl = th + (size_t)kMfmaTile * rank;
+  f16* xs = tl + (size_t)kMfmaTile * rank;
+  const int n_groups = nt * d / 8;
+  hipLaunchKernelGGL((k_xstep<false>), dim3((n_groups + 255) / 256), dim3(256), 0, s, x, nt, d, xs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_mp1<NB>), dim3((rank + kMuRows - 1) / kMuRows, splits), dim3(kMuThreads), 0, s, p1, xs, d,
+                     rank, nt, part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = nt * rank;
+  hipLaunchKernelGGL(k_tsplit, dim3((n + 255) / 256), dim3(256), 0, s, part, splits, nt, rank, t, th, tl);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_mp2<NB>), dim3((d_ff + kMuRows - 1) / kMuRows), dim3(kMuThreads), 0, s, p2, c, th, tl, rank,
+                     d_ff, nt, theta, mask, logits);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool mfma_path(int wtype, int d, int n_tok) {
@@ -469,13 +822,56 @@ bool mfma_path(int wtype, int d, int n_tok) {
 void mfma_workspace(int wtype, int d, int d_ff, int n_tok, size_t* h_bytes, size_t* part_bytes) {
   const int nt = n_tok < kMfmaTile ? n_tok : kMfmaTile;
   const int nb = (nt + 15) / 16;
-  *h_bytes = (size_t)16 * nb * ldh_of(d_ff) * sizeof(f16);
+  (void)nb;
+  *h_bytes = h_region(d_ff, 4) + (size_t)kMfmaTile * d * sizeof(f16);
   *part_bytes = (size_t)mfma_chunks(wtype) * nt * d * sizeof(float);
 }
 
 hipError_t launch_sparse_ffn_mfma(const SparseArgs& a, hipStream_t s) {
   if (a.wtype == 2) return run_mall<Q4>(a, s);
   return run_mall<f16>(a, s);
+}
+
+}  // namespace pi
+
+namespace pi {
+
+// From 3 tokens on, the matrix cores beat the VALU predictor (whose second
+// stage re-reads t from LDS for every weight).  The choice depends only on
+// the predictor and n_tok, so pi_predict and pi_layer always agree.
+bool pred_mfma_path(int wtype, int d, int rank, int n_tok) {
+  return wtype == 1 && d % kMuK == 0 && rank % kMuK == 0 && n_tok > 2;
+}
+
+size_t pred_mfma_part_bytes(int d, int rank, int) {
+  return up256((size_t)pred_splits(d) * kMfmaTile * rank * sizeof(float)) +
+         (2 * (size_t)kMfmaTile * rank + (size_t)kMfmaTile * d) * sizeof(f16);
+}
+
+hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
+                               int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
+                               hipStream_t s) {
+  for (int t0 = 0; t0 < n_tok; t0 += kMfmaTile) {
+    const int nt = n_tok - t0 < kMfmaTile ? n_tok - t0 : kMfmaTile;
+    const f16* xt = static_cast<const f16*>(x) + (size_t)t0 * d;
+    float* tt = t + (size_t)t0 * rank;
+    uint8_t* mt = mask + (size_t)t0 * d_ff;
+    float* lt = logits ? logits + (size_t)t0 * d_ff : nullptr;
+    const f16* a = static_cast<const f16*>(p1);
+    const f16* b = static_cast<const f16*>(p2);
+    char* wsp = static_cast<char*>(ws);
+    hipError_t e;
+    if (nt <= 16)
+      e = run_ptile<1>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+    else if (nt <= 32)
+      e = run_ptile<2>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+    else if (nt <= 48)
+      e = run_ptile<3>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+    else
+      e = run_ptile<4>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pi

@@ -41,35 +41,41 @@ def _row_bytes(cfg):
     return cfg.d_model * ELEM_BYTES[cfg.wtype]
 
 
-def bytes_predict(cfg):
-    """Algorithmic bytes of one pi_predict call at batch 1."""
+def bytes_predict(cfg, n_tok=1):
+    """Algorithmic bytes of one pi_predict call: both predictor matrices and
+    its bias, x, and the masks."""
     eb = ELEM_BYTES[cfg.pred_wtype]
-    return (cfg.rank * cfg.d_model + cfg.d_ff * cfg.rank) * eb + 4 * cfg.d_ff + cfg.d_model * eb + cfg.d_ff
+    return (cfg.rank * cfg.d_model + cfg.d_ff * cfg.rank) * eb + 4 * cfg.d_ff + n_tok * (cfg.d_model * eb + cfg.d_ff)
 
 
-def bytes_compact(cfg, cnt):
-    return cfg.d_ff + 4 * cnt + 4
+def bytes_compact(cfg, cnt, n_tok=1):
+    return n_tok * cfg.d_ff + 4 * cnt + 4
 
 
-def bytes_gather(cfg, cnt):
-    """Algorithmic bytes of one pi_sparse_ffn call at batch 1: the active
-    weight rows, their biases and list entries, x and y."""
+def bytes_gather(cfg, cnt, n_tok=1):
+    """Algorithmic bytes of one pi_sparse_ffn call: the active weight rows
+    (each read once for all tokens), their biases and list entries, x and y."""
     xb = 2 if cfg.wtype == "q4_0" else ELEM_BYTES[cfg.wtype]
-    return cnt * cfg.n_mat * _row_bytes(cfg) + 8 * cnt + cfg.d_model * xb + 4 * cfg.d_model
+    return cnt * cfg.n_mat * _row_bytes(cfg) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model)
 
 
 def bytes_active(cfg, cnt):
     return cnt * cfg.n_mat * _row_bytes(cfg)
 
 
-def bytes_layer(cfg, cnt):
-    """Algorithmic bytes of one pi_layer call at batch 1: both predictor
-    matrices and its bias, x, the active FFN rows with their biases, the
-    active list and y."""
+def bytes_layer(cfg, cnt, n_tok=1):
+    """Algorithmic bytes of one pi_layer call: both predictor matrices and
+    its bias, x, the active FFN rows (once for all tokens) with their biases,
+    the active list and y."""
     eb = ELEM_BYTES[cfg.pred_wtype]
     xb = 2 if cfg.wtype == "q4_0" else ELEM_BYTES[cfg.wtype]
-    return ((cfg.rank * cfg.d_model + cfg.d_ff * cfg.rank) * eb + 4 * cfg.d_ff + cfg.d_model * xb
-            + bytes_active(cfg, cnt) + 8 * cnt + 4 * cfg.d_model)
+    return ((cfg.rank * cfg.d_model + cfg.d_ff * cfg.rank) * eb + 4 * cfg.d_ff
+            + bytes_active(cfg, cnt) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model))
+
+
+def flops_ffn(cfg, cnt, n_tok):
+    """Multiply-adds x 2 of the sparse FFN over cnt listed neurons."""
+    return 2.0 * cnt * cfg.n_mat * cfg.d_model * n_tok
 
 
 def _time_graph(graph, reps, stream):
@@ -93,28 +99,50 @@ def cpu_baseline(cfg, layers, xs_host, budget_s=20.0, max_samples=64):
         threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:       # pragma: no cover - threadpoolctl missing
         threads = os.cpu_count() or 1
-    done, t_total, samples = 0, 0.0, []
+    # xs_host: [steps][layers][batch][d]; one oracle call takes one step's batch of one layer
+    done, calls, t_total = 0, 0, 0.0
     for li, hl in enumerate(layers):
         for tok in range(xs_host.shape[0]):
             x = xs_host[tok, li]
             t0 = time.perf_counter()
             oracle.layer(x, hl["p1"], hl["p2"], hl["c"], cfg.tau, **hl["ffn"])
             t_total += time.perf_counter() - t0
-            done += 1
-            samples.append((li, tok))
-            if t_total > budget_s or done >= max_samples:
+            done += x.shape[0]
+            calls += 1
+            if t_total > budget_s or calls >= max_samples:
                 break
-        if t_total > budget_s or done >= max_samples:
+        if t_total > budget_s or calls >= max_samples:
             break
     return {
         "value": done / t_total,
         "unit": "layer-tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"oracle layer (predict, compact, sparse FFN; float64) on {done} layer-tokens "
-                  f"(layers 0-{len(layers) - 1}, tokens 0-{xs_host.shape[0] - 1}) of the same stack, "
+        "sample": f"oracle layer (predict, compact, sparse FFN; float64) on {done} layer-tokens in {calls} calls "
+                  f"(layers 0-{len(layers) - 1}, steps 0-{xs_host.shape[0] - 1}, batch {xs_host.shape[2]}) "
+                  f"of the same stack, "
                   f"{t_total:.1f} s on {os.cpu_count()} host cores ({threads} BLAS threads)",
     }
+
+
+def _tile(cfg):
+    """Tokens per pass of the list path (fp16 / fp32: 8; Q4_0: x tile <= 32 KB)."""
+    if cfg.wtype != "q4_0":
+        return 8
+    t = 8
+    while t > 1 and t * cfg.d_model * 2 > 32768:
+        t //= 2
+    return t
+
+
+def _kernels(cfg, n_tok):
+    """Kernel names of one pi_layer call on this workload (labels only)."""
+    q4 = cfg.wtype == "q4_0"
+    if n_tok <= _tile(cfg) and n_tok <= 8:
+        return f"k_pred1 + k_pred_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
+    if cfg.wtype in ("f16", "q4_0") and cfg.d_model % 128 == 0:
+        return "k_pred1 + k_pred2 + k_compact + k_mup + k_mdown + k_merge"
+    return f"k_pred1 + k_pred2 + k_compact + k_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
 
 
 def main(argv=None):
@@ -123,9 +151,11 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="falcon40b")
+    ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (their masks are OR-ed)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--reps", type=int, default=20, help="replays for the per-call timing graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prompt", action="store_true", help="skip the multi-token prompt measurement")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,9 +172,10 @@ def main(argv=None):
     pi.load_library()
     cfg = workload.get_config(args.workload)
     dev = torch.device("cuda")
-    L, d, f = cfg.n_layers, cfg.d_model, cfg.d_ff
+    L, d, f, B = cfg.n_layers, cfg.d_model, cfg.d_ff, args.batch
     T = args.warmup + args.steps
     xdt = torch.float16 if cfg.x_dtype == "f16" else torch.float32
+    n_prompt = cfg.prompt if (B == 1 and cfg.prompt > 0 and not args.no_prompt) else 0
 
     n_base_layers, n_base_tok = 4, 16
     q4 = cfg.wtype == "q4_0"
@@ -164,30 +195,30 @@ def main(argv=None):
         layers.append(lw)
         if (li + 1) % 10 == 0:
             print(f"[bench] generated layer {li + 1}/{L}", file=sys.stderr, flush=True)
-    x_all = torch.empty((T, L, d), dtype=xdt, device=dev)
+    # decode inputs: T steps x L layers x B tokens, already in HBM
+    x_all = torch.empty((T, L, B, d), dtype=xdt, device=dev)
     for li in range(L):
-        x_all[:, li] = workload.make_tokens(cfg, li, T, dev, args.seed)
+        x_all[:, li] = workload.make_tokens(cfg, li, T * B, dev, args.seed).view(T, B, d)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
 
     preds = [pi.Predictor(lw["p1"], lw["p2"], lw["c"]) for lw in layers]
     ffns = [pi.FFN(lw["w_up"], lw["w_down_t"], cfg.act, b_up=lw.get("b_up"), w_gate=lw.get("w_gate"),
                    b_gate=lw.get("b_gate"), d_model=d if q4 else None) for lw in layers]
-    ws_bytes = pi.workspace_bytes(preds[0], ffns[0], 1)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    x_stage = torch.zeros((L, d), dtype=xdt, device=dev)
-    y_all = torch.empty((L, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(pi.workspace_bytes(preds[0], ffns[0], B), dtype=torch.uint8, device=dev)
+    x_stage = torch.zeros((L, B, d), dtype=xdt, device=dev)
+    y_all = torch.empty((L, B, d), dtype=torch.float32, device=dev)
 
     stream = torch.cuda.Stream()
     # ---------------- the decode step graph ----------------
     with torch.cuda.stream(stream):
         for li in range(L):   # eager run once before capture (also loads code objects)
-            pi.layer(preds[li], ffns[li], x_stage[li:li + 1], cfg.tau, y_all[li:li + 1], ws=ws)
+            pi.layer(preds[li], ffns[li], x_stage[li], cfg.tau, y_all[li], ws=ws)
     torch.cuda.synchronize()
     g_step = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_step, stream=stream):
         for li in range(L):
-            pi.layer(preds[li], ffns[li], x_stage[li:li + 1], cfg.tau, y_all[li:li + 1], ws=ws)
+            pi.layer(preds[li], ffns[li], x_stage[li], cfg.tau, y_all[li], ws=ws)
     torch.cuda.synchronize()
 
     def step(t):
@@ -208,19 +239,20 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    layer_tok_s = args.steps * L / (ms_total / 1e3)
+    layer_tok_s = args.steps * L * B / (ms_total / 1e3)
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
-    # ---------------- per-(layer, token) counts of the timed steps ----------------
-    mask = torch.empty((L, f), dtype=torch.uint8, device=dev)
+    # ---------------- per-(layer, step) list lengths of the timed steps ----------------
+    mask = torch.empty((L, B, f), dtype=torch.uint8, device=dev)
     idx = torch.empty((L, f), dtype=torch.int32, device=dev)
     cnt = torch.zeros((L,), dtype=torch.int32, device=dev)
     cnt_hist = torch.empty((args.steps, L), dtype=torch.int32, device=dev)
-    ws_p = torch.empty(pi.workspace_bytes(preds[0], None, 1), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(pi.workspace_bytes(preds[0], None, B), dtype=torch.uint8, device=dev)
     g_pc = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_pc, stream=stream):
         for li in range(L):
-            pi.predict(preds[li], x_stage[li:li + 1], cfg.tau, mask[li:li + 1], ws=ws_p)
-            pi.compact(mask[li:li + 1], idx[li], cnt[li:li + 1])
+            pi.predict(preds[li], x_stage[li], cfg.tau, mask[li], ws=ws_p)
+            pi.compact(mask[li], idx[li], cnt[li:li + 1])
     with torch.cuda.stream(stream):
         for t in range(args.warmup, T):
             x_stage.copy_(x_all[t], non_blocking=True)
@@ -231,26 +263,26 @@ def main(argv=None):
     cnt_mean = float(counts.mean())
 
     # ---------------- per-call timing: predict, compact, sparse FFN ----------------
-    # inputs of the last timed token; idx/count of every layer from g_pc
-    ws_s = torch.empty(pi.workspace_bytes(None, ffns[0], 1), dtype=torch.uint8, device=dev)
+    # inputs of the last timed step; idx/count of every layer from g_pc
+    ws_s = torch.empty(pi.workspace_bytes(None, ffns[0], B), dtype=torch.uint8, device=dev)
     g_pred, g_comp, g_sp = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_pred, stream=stream):
         for li in range(L):
-            pi.predict(preds[li], x_stage[li:li + 1], cfg.tau, mask[li:li + 1], ws=ws_p)
+            pi.predict(preds[li], x_stage[li], cfg.tau, mask[li], ws=ws_p)
     with torch.cuda.graph(g_comp, stream=stream):
         for li in range(L):
-            pi.compact(mask[li:li + 1], idx[li], cnt[li:li + 1])
+            pi.compact(mask[li], idx[li], cnt[li:li + 1])
     with torch.cuda.graph(g_sp, stream=stream):
         for li in range(L):
-            pi.sparse_ffn(ffns[li], x_stage[li:li + 1], idx[li], cnt[li:li + 1], y_all[li:li + 1], ws=ws_s)
+            pi.sparse_ffn(ffns[li], x_stage[li], idx[li], cnt[li:li + 1], y_all[li], ws=ws_s)
     with torch.cuda.stream(stream):
         ms_pred = _time_graph(g_pred, args.reps, stream) / L
         ms_comp = _time_graph(g_comp, args.reps, stream) / L
         ms_sp = _time_graph(g_sp, args.reps, stream) / L
     last_cnt = cnt.cpu().numpy().astype(np.int64)
-    b_pred = bytes_predict(cfg)
-    b_comp = float(np.mean([bytes_compact(cfg, c) for c in last_cnt]))
-    b_sp = float(np.mean([bytes_gather(cfg, c) for c in last_cnt]))
+    b_pred = bytes_predict(cfg, B)
+    b_comp = float(np.mean([bytes_compact(cfg, c, B) for c in last_cnt]))
+    b_sp = float(np.mean([bytes_gather(cfg, c, B) for c in last_cnt]))
     b_act = float(np.mean([bytes_active(cfg, c) for c in last_cnt]))
 
     def roof(kernels, b, ms):
@@ -259,16 +291,17 @@ def main(argv=None):
                 "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                 "bytes_per_launch": int(b), "avg_launch_us": round(ms * 1e3, 3)}
 
-    # whole-layer bytes per layer-token, averaged over the timed steps
-    b_layer = float(np.mean([bytes_layer(cfg, c) for c in counts.flat]))
+    # whole-layer bytes per layer call, averaged over the timed steps
+    b_layer = float(np.mean([bytes_layer(cfg, c, B) for c in counts.flat]))
     ms_layer = ms_step / L
-    dn = "k_down_q4" if q4 else "k_down"
-    layer_roof = roof(f"pi_layer (k_pred1 + k_pred_up + {dn} + k_merge)", b_layer, ms_layer)
+    kern = _kernels(cfg, B)
+    gather_kern = kern.split(" + ", 3)[-1] if "k_pred_up" not in kern else kern.replace("k_pred1 + k_pred_up", "k_up")
+    layer_roof = roof(f"pi_layer ({kern})", b_layer, ms_layer)
     parts = {
         "predict": roof("pi_predict (k_pred1 + k_pred2)", b_pred, ms_pred),
         "compact": {"kernel": "pi_compact (k_compact)", "avg_launch_us": round(ms_comp * 1e3, 3),
                     "bytes_per_launch": int(b_comp)},
-        "gather": roof(f"pi_sparse_ffn (k_up + {dn} + k_merge)", b_sp, ms_sp),
+        "gather": roof(f"pi_sparse_ffn ({gather_kern})", b_sp, ms_sp),
     }
     parts["gather"]["active_weight_gbps"] = round(b_act / (ms_sp * 1e-3) / 1e9, 1)
     parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
@@ -286,9 +319,9 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": cfg.wtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name} decode batch 1", "d_model": d, "d_ff": f, "layers": L,
-                   "rank": cfg.rank, "act": cfg.act, "weights": cfg.wtype, "mean_density": cfg.rho,
-                   "parallelism": "none (1 GPU)"},
+        "config": {"workload": f"{cfg.name} decode batch {B}", "d_model": d, "d_ff": f, "layers": L,
+                   "rank": cfg.rank, "act": cfg.act, "weights": cfg.wtype, "batch": B,
+                   "mean_density": cfg.rho, "parallelism": "none (1 GPU)"},
         "roofline": layer_roof,
         "roofline_parts": parts,
         "count_mean": round(cnt_mean, 1),
@@ -296,6 +329,60 @@ def main(argv=None):
         "count_max": int(counts.max()),
         "gen_seconds": round(t_gen, 1),
     }
+
+    # ---------------- multi-token prompt: per-token masks OR-ed, matrix-core path ----------------
+    if n_prompt:
+        n = n_prompt
+        x_pr = torch.empty((L, n, d), dtype=xdt, device=dev)
+        for li in range(L):
+            x_pr[li] = workload.make_tokens(cfg, li, n, dev, args.seed, stream=1)
+        y_pr = torch.empty((L, n, d), dtype=torch.float32, device=dev)
+        ws_m = torch.empty(pi.workspace_bytes(preds[0], ffns[0], n), dtype=torch.uint8, device=dev)
+        mask_m = torch.empty((L, n, f), dtype=torch.uint8, device=dev)
+        idx_m = torch.empty((L, f), dtype=torch.int32, device=dev)
+        cnt_m = torch.zeros((L,), dtype=torch.int32, device=dev)
+        ws_mp = torch.empty(pi.workspace_bytes(preds[0], None, n), dtype=torch.uint8, device=dev)
+        ws_ms = torch.empty(pi.workspace_bytes(None, ffns[0], n), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            for li in range(L):
+                pi.predict(preds[li], x_pr[li], cfg.tau, mask_m[li], ws=ws_mp)
+                pi.compact(mask_m[li], idx_m[li], cnt_m[li:li + 1])
+                pi.layer(preds[li], ffns[li], x_pr[li], cfg.tau, y_pr[li], ws=ws_m)
+        torch.cuda.synchronize()
+        g_ml, g_mp, g_ms = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_ml, stream=stream):
+            for li in range(L):
+                pi.layer(preds[li], ffns[li], x_pr[li], cfg.tau, y_pr[li], ws=ws_m)
+        with torch.cuda.graph(g_mp, stream=stream):
+            for li in range(L):
+                pi.predict(preds[li], x_pr[li], cfg.tau, mask_m[li], ws=ws_mp)
+        with torch.cuda.graph(g_ms, stream=stream):
+            for li in range(L):
+                pi.sparse_ffn(ffns[li], x_pr[li], idx_m[li], cnt_m[li:li + 1], y_pr[li], ws=ws_ms)
+        reps = max(2, args.reps // 4)
+        with torch.cuda.stream(stream):
+            ms_ml = _time_graph(g_ml, reps, stream) / L
+            ms_mp = _time_graph(g_mp, reps, stream) / L
+            ms_ms = _time_graph(g_ms, reps, stream) / L
+        uc = cnt_m.cpu().numpy().astype(np.int64)
+        b_ml = float(np.mean([bytes_layer(cfg, c, n) for c in uc]))
+        b_ms = float(np.mean([bytes_gather(cfg, c, n) for c in uc]))
+        fl = float(np.mean([flops_ffn(cfg, c, n) for c in uc]))
+        tflops = fl / (ms_ms * 1e-3) / 1e12
+        mk = _kernels(cfg, n)
+        out["multi_token"] = {
+            "what": f"one prompt of {n} tokens per layer, per-token masks OR-ed into one list",
+            "n_tok": n,
+            "union_count_mean": round(float(uc.mean()), 1),
+            "layer_tokens_per_s": round(n / (ms_ml * 1e-3), 1),
+            "layer": roof(f"pi_layer ({mk})", b_ml, ms_ml),
+            "predict": roof("pi_predict (k_pred1 + k_pred2)", bytes_predict(cfg, n), ms_mp),
+            "gather": roof(f"pi_sparse_ffn ({mk.split(' + ', 3)[-1]})", b_ms, ms_ms),
+            "gather_mfma": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                            "frac": round(tflops / 2500.0, 4), "flops_per_launch": fl},
+        }
+        print(f"[bench] prompt {n}: layer {ms_ml * 1e3:.1f} us, gather {ms_ms * 1e3:.1f} us", file=sys.stderr,
+              flush=True)
 
     if not args.no_cpu_baseline:
         import oracle  # the baseline leg is the only user of the oracle here

@@ -89,6 +89,30 @@ def test_predict(dtype, d, r, f, n_tok, tau):
     assert set(np.unique(host(mask))) <= {0, 1}
 
 
+@pytest.mark.parametrize("d,r,f", [(1024, 128, 1001), (8192, 1024, 4000)])
+@pytest.mark.parametrize("n_tok", [3, 16, 17, 64, 70])
+def test_predict_mfma(d, r, f, n_tok):
+    # fp16 predictor with 3 or more tokens: the matrix-core predictor (t split
+    # into fp16 high and low parts for the second product).
+    tau = 0.4
+    g = torch.Generator(device="cuda").manual_seed(d + r + f + 3 * n_tok)
+    p1 = (torch.randn((r, d), generator=g, device="cuda") * 0.02).half()
+    p2 = (torch.randn((f, r), generator=g, device="cuda") * 0.02).half()
+    c = (torch.randn(f, generator=g, device="cuda") * 0.01).float()
+    x = torch.randn((n_tok, d), generator=g, device="cuda").half()
+    pred = pi.Predictor(p1, p2, c)
+    mask = torch.empty((n_tok, f), dtype=torch.uint8, device="cuda")
+    logits = torch.empty((n_tok, f), dtype=torch.float32, device="cuda")
+    pi.predict(pred, x, tau, mask, logits)
+    mask2 = torch.empty_like(mask)
+    pi.predict(pred, x, tau, mask2)                 # without logits: same masks
+    ref_l, _ = oracle.predict(host(x), host(p1), host(p2), host(c), tau)
+    err = np.abs(host(logits).astype(np.float64) - ref_l)
+    assert err.max() <= 1e-5 + 1e-5 * np.abs(ref_l).max()
+    check_mask(host(mask), ref_l, tau, "predict mfma")
+    assert torch.equal(mask, mask2)
+
+
 # ---------------------------------------------------------------------------
 # Sparse FFN over a given list
 # ---------------------------------------------------------------------------
