@@ -43,65 +43,6 @@ __device__ __forceinline__ float activate(float up, float gate) {
   return ACT == ACT_RELU2 ? r * r : r;
 }
 
-// ---------------------------------------------------------------------------
-// One neuron's up projection for nt tokens, computed by a whole wave:
-// hv[j] = act(w_up[i] . x[j] (+ bias), w_gate[i] . x[j] + bias).  Lane l
-// takes 16-byte chunks l, l+64, ... of the row; sum order: lane chunk order,
-// then the wave butterfly, so every lane ends with the same hv.  x comes from
-// LDS (XL: [NT][d/E] 16-byte chunks staged by the workgroup) or from global
-// memory.
-// ---------------------------------------------------------------------------
-constexpr int kUpChunks = 16;   // chunks per lane per pass: 16 KB of row per wave
-
-template <typename W, int ACT, int NT, bool XL>
-__device__ __forceinline__ void row_up(const W* __restrict__ w_up, const W* __restrict__ w_gate, float b, int i,
-                                       int d, const char* __restrict__ xb, const u32x4* x_lds, int nt, int lane,
-                                       float (&hv)[NT]) {
-  constexpr int E = 16 / sizeof(W);
-  constexpr bool GATED = ACT == ACT_REGLU;
-  const int nch = d / E;
-  const char* up = reinterpret_cast<const char*>(w_up + (size_t)i * d);
-  const char* gt = GATED ? reinterpret_cast<const char*>(w_gate + (size_t)i * d) : nullptr;
-  float au[NT], ag[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) au[j] = ag[j] = 0.f;
-  for (int pass = 0; pass < nch; pass += kWave * kUpChunks) {
-    u32x4 wu[kUpChunks], wg[GATED ? kUpChunks : 1];
-#pragma unroll
-    for (int m = 0; m < kUpChunks; ++m) {
-      const int ch = pass + lane + kWave * m;
-      const bool ok = ch < nch;
-      wu[m] = ok ? ld_nt(up + (size_t)ch * 16) : u32x4{0, 0, 0, 0};
-      if (GATED) wg[m] = ok ? ld_nt(gt + (size_t)ch * 16) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if (j < nt) {
-        const char* xr = xb + (size_t)j * d * sizeof(W);
-#pragma unroll
-        for (int m = 0; m < kUpChunks; ++m) {
-          const int ch = pass + lane + kWave * m;
-          if (ch < nch) {
-            const u32x4 xv = XL ? x_lds[j * nch + ch] : ld16(xr + (size_t)ch * 16);
-            au[j] = dotc<W>(wu[m], xv, au[j]);
-            if (GATED) ag[j] = dotc<W>(wg[m], xv, ag[j]);
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    if (j < nt) {
-      const float u = wave_sum(au[j]);
-      const float g = GATED ? wave_sum(ag[j]) : 0.f;
-      hv[j] = GATED ? activate<ACT>(u, g + b) : activate<ACT>(u + b, 0.f);
-    } else {
-      hv[j] = 0.f;
-    }
-  }
-}
-
 // Stage the token tile of x ([nt][d] elements, 16-byte chunks) into LDS.
 template <typename W>
 __device__ __forceinline__ void stage_x(const char* __restrict__ xb, u32x4* x_lds, int nt, int d) {
@@ -137,81 +78,124 @@ __device__ __forceinline__ float dot_q4(u32x4 cw, const u32x4 (&xq)[4]) {
   return acc;
 }
 
-constexpr int kUpBlocks = 8;   // Q4 blocks per lane per pass (512 blocks = 16384 weights per pass)
+// ---------------------------------------------------------------------------
+// Row dots in a fixed order.  A row's units -- 16-byte chunks of fp16 or fp32
+// weights, or Q4_0 blocks -- are split into 4 parts, part q = units
+// [n*q/4, n*(q+1)/4).  In a part, lane l adds the units c_q + l, c_q + l + 64,
+// ... in order; the lane sums are added over the wave (butterfly, so every
+// lane holds the same bits); the 4 part sums are added in order 0..3.  The
+// list path computes the 4 parts of a row in one wave; the layer path gives
+// part q of every active row of a workgroup to its wave q.  Both get the same
+// bits, and a workgroup with many active rows keeps all 4 waves loading.
+// ---------------------------------------------------------------------------
+template <typename WF>
+__device__ __forceinline__ int row_units(int d) {
+  return std::is_same<WF, Q4>::value ? d / 32 : d / (16 / (int)sizeof(WF));
+}
 
-// One neuron's up projection with Q4_0 weights; same structure and sum order
-// rules as row_up: lane l takes blocks l, l+64, ...; each block's sum is
-// scaled by its fp16 scale and added in block order; then the wave butterfly.
-template <int ACT, int NT, bool XL>
-__device__ __forceinline__ void row_up_q4(const uint8_t* __restrict__ w_up, const uint8_t* __restrict__ w_gate,
-                                          size_t scale_off, float b, int i, int d, const char* __restrict__ xb,
-                                          const u32x4* x_lds, int nt, int lane, float (&hv)[NT]) {
-  constexpr bool GATED = ACT == ACT_REGLU;
-  const int nb = d / 32;
-  const int nch = d / 8;                       // 16-byte activation chunks per token
-  const uint8_t* cu = w_up + (size_t)i * nb * 16;
-  const f16* su = reinterpret_cast<const f16*>(w_up + scale_off) + (size_t)i * nb;
-  const uint8_t* cg = GATED ? w_gate + (size_t)i * nb * 16 : nullptr;
-  const f16* sg = GATED ? reinterpret_cast<const f16*>(w_gate + scale_off) + (size_t)i * nb : nullptr;
-  float au[NT], ag[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) au[j] = ag[j] = 0.f;
-  for (int pass = 0; pass < nb; pass += kWave * kUpBlocks) {
-    u32x4 wu[kUpBlocks], wg[GATED ? kUpBlocks : 1];
-    float du[kUpBlocks], dg[GATED ? kUpBlocks : 1];
-#pragma unroll
-    for (int m = 0; m < kUpBlocks; ++m) {
-      const int blk = pass + lane + kWave * m;
-      const bool ok = blk < nb;
-      wu[m] = ok ? ld_nt(cu + (size_t)blk * 16) : u32x4{0, 0, 0, 0};
-      du[m] = ok ? (float)su[blk] : 0.f;
-      if (GATED) {
-        wg[m] = ok ? ld_nt(cg + (size_t)blk * 16) : u32x4{0, 0, 0, 0};
-        dg[m] = ok ? (float)sg[blk] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if (j < nt) {
-        const char* xr = xb + (size_t)j * d * sizeof(f16);
-#pragma unroll
-        for (int m = 0; m < kUpBlocks; ++m) {
-          const int blk = pass + lane + kWave * m;
-          if (blk < nb) {
-            u32x4 xq[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              xq[k] = XL ? x_lds[j * nch + 4 * blk + k] : ld16(xr + (size_t)(4 * blk + k) * 16);
-            au[j] = __builtin_fmaf(du[m], dot_q4(wu[m], xq), au[j]);
-            if (GATED) ag[j] = __builtin_fmaf(dg[m], dot_q4(wg[m], xq), ag[j]);
-          }
-        }
-      }
-    }
+struct UnitW {
+  u32x4 w;
+  float sc;     // Q4_0 block scale
+};
+
+template <typename WF>
+__device__ __forceinline__ UnitW load_unit(const void* w, size_t scale_off, int row, int u, int d, bool ok) {
+  UnitW r;
+  if constexpr (std::is_same<WF, Q4>::value) {
+    const size_t blk = (size_t)row * (d / 32) + u;
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    r.w = ok ? ld_nt(wb + blk * 16) : u32x4{0, 0, 0, 0};
+    r.sc = ok ? (float)reinterpret_cast<const f16*>(wb + scale_off)[blk] : 0.f;
+  } else {
+    r.w = ok ? ld_nt(static_cast<const char*>(w) + (size_t)row * d * sizeof(WF) + (size_t)u * 16)
+             : u32x4{0, 0, 0, 0};
+    r.sc = 0.f;
   }
+  return r;
+}
+
+// acc + unit u . x, for one token: xr is its row in global memory, xl in LDS.
+template <typename WF, bool XL>
+__device__ __forceinline__ float unit_dot(const UnitW& U, int u, const char* xr, const u32x4* xl, float acc) {
+  if constexpr (std::is_same<WF, Q4>::value) {
+    u32x4 xq[4];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    if (j < nt) {
-      const float u = wave_sum(au[j]);
-      const float g = GATED ? wave_sum(ag[j]) : 0.f;
-      hv[j] = GATED ? activate<ACT>(u, g + b) : activate<ACT>(u + b, 0.f);
-    } else {
-      hv[j] = 0.f;
-    }
+    for (int k = 0; k < 4; ++k) xq[k] = XL ? xl[4 * u + k] : ld16(xr + (size_t)(4 * u + k) * 16);
+    return __builtin_fmaf(U.sc, dot_q4(U.w, xq), acc);
+  } else {
+    return dotc<WF>(U.w, XL ? xl[u] : ld16(xr + (size_t)u * 16), acc);
   }
 }
 
-// Up projection of neuron i for any FFN weight type.
-template <typename WF, int ACT, int NT, bool XL>
-__device__ __forceinline__ void row_up_any(const void* w_up, const void* w_gate, size_t scale_off, float b, int i,
-                                           int d, const char* xb, const u32x4* x_lds, int nt, int lane,
-                                           float (&hv)[NT]) {
-  if constexpr (std::is_same<WF, Q4>::value)
-    row_up_q4<ACT, NT, XL>(static_cast<const uint8_t*>(w_up), static_cast<const uint8_t*>(w_gate), scale_off, b, i,
-                           d, xb, x_lds, nt, lane, hv);
-  else
-    row_up<WF, ACT, NT, XL>(static_cast<const WF*>(w_up), static_cast<const WF*>(w_gate), b, i, d, xb, x_lds, nt,
-                            lane, hv);
+constexpr int kPartUnits = 4;   // units per lane per pass of a part (d = 8192 fp16: one pass)
+
+// pu[s][j] = part parts[s] of row rows[s] of w_up dotted with token j, summed
+// over the wave (pg: the same for w_gate).  Entries with ok[s] false give 0.
+// All loads of a pass (S parts x kPartUnits units) are in flight together.
+template <typename WF, bool GATED, int NT, bool XL, int S>
+__device__ __forceinline__ void part_dots(const void* w_up, const void* w_gate, size_t scale_off,
+                                          const int (&rows)[S], const int (&parts)[S], const bool (&ok)[S], int d,
+                                          const char* xb, const u32x4* x_lds, int nt, int lane, float (&pu)[S][NT],
+                                          float (&pg)[S][NT]) {
+  using X = typename FfnTraits<WF>::X;
+  const int n = row_units<WF>(d);
+  const int xch = d / (16 / (int)sizeof(X));   // 16-byte chunks of one token's x
+  int c0[S], c1[S];
+  float au[S][NT], ag[S][NT];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    c0[s] = n * parts[s] / 4;
+    c1[s] = n * (parts[s] + 1) / 4;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) au[s][j] = ag[s][j] = 0.f;
+  }
+  const int len = (n + 3) / 4;
+  for (int p = 0; p < len; p += kWave * kPartUnits) {
+    UnitW wu[S][kPartUnits], wg[GATED ? S : 1][kPartUnits];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int m = 0; m < kPartUnits; ++m) {
+        const int u = c0[s] + p + lane + kWave * m;
+        const bool v = ok[s] && u < c1[s];
+        wu[s][m] = load_unit<WF>(w_up, scale_off, rows[s], u, d, v);
+        if constexpr (GATED) wg[s][m] = load_unit<WF>(w_gate, scale_off, rows[s], u, d, v);
+      }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (j < nt) {
+        const char* xr = xb + (size_t)j * d * sizeof(X);
+        const u32x4* xl = x_lds + j * xch;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int m = 0; m < kPartUnits; ++m) {
+            const int u = c0[s] + p + lane + kWave * m;
+            if (ok[s] && u < c1[s]) {
+              au[s][j] = unit_dot<WF, XL>(wu[s][m], u, xr, xl, au[s][j]);
+              if constexpr (GATED) ag[s][j] = unit_dot<WF, XL>(wg[s][m], u, xr, xl, ag[s][j]);
+            }
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      pu[s][j] = wave_sum(au[s][j]);
+      pg[s][j] = GATED ? wave_sum(ag[s][j]) : 0.f;
+    }
+}
+
+// h from the 4 part sums (in order) and the bias (b_up for ReLU / ReLU^2,
+// b_gate for ReGLU).
+template <int ACT>
+__device__ __forceinline__ float combine_parts(float u0, float u1, float u2, float u3, float g0, float g1, float g2,
+                                               float g3, float b) {
+  const float u = ((u0 + u1) + u2) + u3;
+  if (ACT == ACT_REGLU) return activate<ACT>(u, (((g0 + g1) + g2) + g3) + b);
+  return activate<ACT>(u + b, 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,17 +229,22 @@ __global__ __launch_bounds__(kUpThreads) void k_up(const void* __restrict__ w_up
   for (int k = k_first; k < cnt; k += n_waves) {
     const int i = i_next;
     i_next = k + n_waves < cnt ? idx[k + n_waves] : -1;
-    float hv[NT];
-    if ((unsigned)i < (unsigned)d_ff) {
-      row_up_any<WF, ACT, NT, XL>(w_up, w_gate, scale_off, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) hv[j] = 0.f;   // malformed entry: it adds nothing
-    }
+    const bool valid = (unsigned)i < (unsigned)d_ff;      // a malformed entry adds nothing
+    const int r = valid ? i : 0;
+    const int rows[4] = {r, r, r, r}, parts[4] = {0, 1, 2, 3};
+    const bool ok[4] = {valid, valid, valid, valid};
+    float pu[4][NT], pg[4][NT];
+    part_dots<WF, ACT == ACT_REGLU, NT, XL, 4>(w_up, w_gate, scale_off, rows, parts, ok, d, xb, x_lds, nt, lane, pu,
+                                               pg);
+    const float b = valid && bias ? bias[i] : 0.f;
     if (lane == 0)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        if (j < nt) h[(size_t)j * d_ff + k] = hv[j];
+        if (j < nt)
+          h[(size_t)j * d_ff + k] =
+              valid ? combine_parts<ACT>(pu[0][j], pu[1][j], pu[2][j], pu[3][j], pg[0][j], pg[1][j], pg[2][j],
+                                         pg[3][j], b)
+                    : 0.f;
   }
 }
 
@@ -289,6 +278,7 @@ constexpr int kPURows = kPUThreads / kP2Group * kPUSub;               // 32 neur
 constexpr int kPULoads = 8;                                           // status loads per thread per batch
 constexpr unsigned kReady = 0x80000000u;
 constexpr int kSpinLimit = 1 << 16;
+constexpr int kPUBatch = 4;                                           // rows per phase-C batch (ReLU)
 
 template <typename W, typename WF, int ACT, int NT, bool XL>
 __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2, const float* __restrict__ c,
@@ -303,7 +293,8 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   float* t_lds = smem;
   u32x4* x_lds = reinterpret_cast<u32x4*>(smem + NT * rank);
   __shared__ int act_lds[kPURows];
-  __shared__ float h_lds[NT][kPURows];
+  __shared__ float pu_lds[kPUWaves][kPURows][NT];                     // part sums of phase C
+  __shared__ float pg_lds[ACT == ACT_REGLU ? kPUWaves : 1][kPURows][NT];
   __shared__ int red_lds[kPUWaves];
   const int lane = lane_id();
   const int wave = wave_id();
@@ -349,18 +340,35 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   if (threadIdx.x == 0)
     __hip_atomic_store(&status[wg], kReady | (unsigned)n_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- C: up projection of the active neurons, dealt to the waves ----
-  unsigned long long bits = am;
-  for (int k = 0; bits; ++k) {
-    const int r = __builtin_ctzll(bits);
-    bits &= bits - 1;
-    if ((k & (kPUWaves - 1)) != wave) continue;
-    const int i = seg0 + r;
-    float hv[NT];
-    row_up_any<WF, ACT, NT, XL>(w_up, w_gate, scale_off, bias ? bias[i] : 0.f, i, d, xb, x_lds, nt, lane, hv);
-    if (lane == 0)
+  // ---- C: up projection of the active neurons: wave q computes part q of
+  // every active row, kPUBatch rows at a time with all their loads in flight.
+  {
+    constexpr int S = ACT == ACT_REGLU ? kPUBatch / 2 : kPUBatch;
+    unsigned long long bits = am;                  // the same in every wave
+    while (bits) {
+      int rows[S], parts[S], rr[S];
+      bool ok[S];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) h_lds[j][r] = hv[j];
+      for (int s = 0; s < S; ++s) {
+        ok[s] = bits != 0;
+        rr[s] = ok[s] ? __builtin_ctzll(bits) : 0;
+        bits &= bits - 1;
+        rows[s] = seg0 + rr[s];
+        parts[s] = wave;
+      }
+      float pu[S][NT], pg[S][NT];
+      part_dots<WF, ACT == ACT_REGLU, NT, XL, S>(w_up, w_gate, scale_off, rows, parts, ok, d, xb, x_lds, nt, lane,
+                                                 pu, pg);
+      if (lane == 0)
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+          if (ok[s])
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              pu_lds[wave][rr[s]][j] = pu[s][j];
+              if (ACT == ACT_REGLU) pg_lds[wave][rr[s]][j] = pg[s][j];
+            }
+    }
   }
 
   // ---- D: offset = sum of the earlier workgroups' counts; write the list ----
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
   if (lane == 0) red_lds[wave] = part;
-  __syncthreads();   // also orders the h_lds writes of phase C before their reads below
+  __syncthreads();   // also orders the part sums of phase C before their reads below
   int off = 0;
 #pragma unroll
   for (int w = 0; w < kPUWaves; ++w) off += red_lds[w];
@@ -395,10 +403,19 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
     const bool mine = lane < kPURows && ((am >> lane) & 1ull);
     const int pos = off + __builtin_popcountll(am & ((1ull << lane) - 1ull));
     if (mine) {
-      idx[pos] = seg0 + lane;
+      const int i = seg0 + lane;
+      idx[pos] = i;
+      const float b = bias ? bias[i] : 0.f;
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        if (j < nt) h[(size_t)j * d_ff + pos] = h_lds[j][lane];
+      for (int j = 0; j < NT; ++j) {
+        if (j < nt) {
+          const bool gt = ACT == ACT_REGLU;
+          const float g0 = gt ? pg_lds[0][lane][j] : 0.f, g1 = gt ? pg_lds[1][lane][j] : 0.f;
+          const float g2 = gt ? pg_lds[2][lane][j] : 0.f, g3 = gt ? pg_lds[3][lane][j] : 0.f;
+          h[(size_t)j * d_ff + pos] = combine_parts<ACT>(pu_lds[0][lane][j], pu_lds[1][lane][j], pu_lds[2][lane][j],
+                                                         pu_lds[3][lane][j], g0, g1, g2, g3, b);
+        }
+      }
     }
     if (wg == (int)gridDim.x - 1 && lane == 0) *count = off + n_g;
   }
