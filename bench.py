@@ -22,8 +22,11 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -76,6 +79,44 @@ def bytes_layer(cfg, cnt, n_tok=1):
 def flops_ffn(cfg, cnt, n_tok):
     """Multiply-adds x 2 of the sparse FFN over cnt listed neurons."""
     return 2.0 * cnt * cfg.n_mat * cfg.d_model * n_tok
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_sha256():
+    """sha256 over include/pi.h and the kernel sources, in name order."""
+    files = [os.path.join(ROOT, "include", "pi.h")]
+    d = os.path.join(ROOT, "activation_sparse_rank_amd", "csrc")
+    files += [os.path.join(d, f) for f in sorted(os.listdir(d)) if f.endswith((".hip", ".h"))]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        h.update(b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload):
+    """HBM bytes per dispatch of each kernel, from the committed rocprofv3 PMC
+    summary of this workload (profiles/*_traffic.md), or None when there is
+    none or the kernels have changed since it was taken."""
+    sha = None
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        with open(path) as fh:
+            m = re.search(r"```json\n(.*?)\n```", fh.read(), re.S)
+        if not m:
+            continue
+        data = json.loads(m.group(1))
+        if data.get("workload") != workload:
+            continue
+        sha = sha or kernel_source_sha256()
+        if data.get("source_sha256") != sha:
+            return None
+        fs, ws = data["fetch_scale"], data["write_scale"]
+        return {k: (v["fetch_kib"] * fs + v["write_kib"] * ws) * 1024.0 for k, v in data["kernels"].items()}
+    return None
 
 
 def _time_graph(graph, reps, stream):
@@ -135,14 +176,27 @@ def _tile(cfg):
     return t
 
 
-def _kernels(cfg, n_tok):
-    """Kernel names of one pi_layer call on this workload (labels only)."""
+def _pred_kernels(cfg, n_tok):
+    """Kernels of one pi_predict call (labels only)."""
+    if cfg.pred_wtype == "f16" and cfg.d_model % 128 == 0 and cfg.rank % 128 == 0 and n_tok > 2:
+        return "k_xstep + k_mp1 + k_tsplit + k_mp2"
+    return "k_pred1 + k_pred2"
+
+
+def _ffn_kernels(cfg, n_tok):
+    """Kernels of one pi_sparse_ffn call (labels only)."""
     q4 = cfg.wtype == "q4_0"
-    if n_tok <= _tile(cfg) and n_tok <= 8:
-        return f"k_pred1 + k_pred_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
-    if cfg.wtype in ("f16", "q4_0") and cfg.d_model % 128 == 0:
-        return "k_pred1 + k_pred2 + k_compact + k_mup + k_mdown + k_merge"
-    return f"k_pred1 + k_pred2 + k_compact + k_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
+    if n_tok > _tile(cfg) and cfg.wtype in ("f16", "q4_0") and cfg.d_model % 128 == 0:
+        return "k_xstep + k_mup + k_mdown + k_merge"
+    return f"k_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
+
+
+def _kernels(cfg, n_tok):
+    """Kernels of one pi_layer call (labels only)."""
+    pred = _pred_kernels(cfg, n_tok)
+    if n_tok <= _tile(cfg) and n_tok <= 8 and pred == "k_pred1 + k_pred2":
+        return f"k_pred1 + k_pred_up + {'k_down_q4' if cfg.wtype == 'q4_0' else 'k_down'} + k_merge"
+    return f"{pred} + k_compact + {_ffn_kernels(cfg, n_tok)}"
 
 
 def main(argv=None):
@@ -285,23 +339,31 @@ def main(argv=None):
     b_sp = float(np.mean([bytes_gather(cfg, c, B) for c in last_cnt]))
     b_act = float(np.mean([bytes_active(cfg, c) for c in last_cnt]))
 
+    traffic_table = load_traffic(f"{cfg.name} decode batch {B}")
+
+    def traffic_of(kernels):
+        # measured HBM bytes per call of the kernel set named in the label
+        names = re.findall(r"k_[a-z0-9_]+", kernels)
+        if traffic_table is None or not names or any(k not in traffic_table for k in names):
+            return None
+        return int(sum(traffic_table[k] for k in names))
+
     def roof(kernels, b, ms):
         gbps = b / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "kernel": kernels, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_of(kernels),
                 "bytes_per_launch": int(b), "avg_launch_us": round(ms * 1e3, 3)}
 
     # whole-layer bytes per layer call, averaged over the timed steps
     b_layer = float(np.mean([bytes_layer(cfg, c, B) for c in counts.flat]))
     ms_layer = ms_step / L
     kern = _kernels(cfg, B)
-    gather_kern = kern.split(" + ", 3)[-1] if "k_pred_up" not in kern else kern.replace("k_pred1 + k_pred_up", "k_up")
     layer_roof = roof(f"pi_layer ({kern})", b_layer, ms_layer)
     parts = {
-        "predict": roof("pi_predict (k_pred1 + k_pred2)", b_pred, ms_pred),
+        "predict": roof(f"pi_predict ({_pred_kernels(cfg, B)})", b_pred, ms_pred),
         "compact": {"kernel": "pi_compact (k_compact)", "avg_launch_us": round(ms_comp * 1e3, 3),
                     "bytes_per_launch": int(b_comp)},
-        "gather": roof(f"pi_sparse_ffn ({gather_kern})", b_sp, ms_sp),
+        "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, B)})", b_sp, ms_sp),
     }
     parts["gather"]["active_weight_gbps"] = round(b_act / (ms_sp * 1e-3) / 1e9, 1)
     parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
@@ -376,8 +438,8 @@ def main(argv=None):
             "union_count_mean": round(float(uc.mean()), 1),
             "layer_tokens_per_s": round(n / (ms_ml * 1e-3), 1),
             "layer": roof(f"pi_layer ({mk})", b_ml, ms_ml),
-            "predict": roof("pi_predict (k_pred1 + k_pred2)", bytes_predict(cfg, n), ms_mp),
-            "gather": roof(f"pi_sparse_ffn ({mk.split(' + ', 3)[-1]})", b_ms, ms_ms),
+            "predict": roof(f"pi_predict ({_pred_kernels(cfg, n)})", bytes_predict(cfg, n), ms_mp),
+            "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, n)})", b_ms, ms_ms),
             "gather_mfma": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                             "frac": round(tflops / 2500.0, 4), "flops_per_launch": fl},
         }
