@@ -127,11 +127,14 @@ __device__ __forceinline__ float unit_dot(const UnitW& U, int u, const char* xr,
   }
 }
 
-constexpr int kPartUnits = 4;   // units per lane per pass of a part (d = 8192 fp16: one pass)
+// Units per lane per pass of a part: one pass at d = 8192 (fp16: 256 units
+// per part; Q4_0: 64 blocks per part).
+template <typename WF>
+constexpr int part_units() { return std::is_same<WF, Q4>::value ? 1 : 4; }
 
 // pu[s][j] = part parts[s] of row rows[s] of w_up dotted with token j, summed
 // over the wave (pg: the same for w_gate).  Entries with ok[s] false give 0.
-// All loads of a pass (S parts x kPartUnits units) are in flight together.
+// All loads of a pass (S parts x part_units units) are in flight together.
 template <typename WF, bool GATED, int NT, bool XL, int S>
 __device__ __forceinline__ void part_dots(const void* w_up, const void* w_gate, size_t scale_off,
                                           const int (&rows)[S], const int (&parts)[S], const bool (&ok)[S], int d,
@@ -150,12 +153,13 @@ __device__ __forceinline__ void part_dots(const void* w_up, const void* w_gate, 
     for (int j = 0; j < NT; ++j) au[s][j] = ag[s][j] = 0.f;
   }
   const int len = (n + 3) / 4;
-  for (int p = 0; p < len; p += kWave * kPartUnits) {
-    UnitW wu[S][kPartUnits], wg[GATED ? S : 1][kPartUnits];
+  constexpr int PU = part_units<WF>();
+  for (int p = 0; p < len; p += kWave * PU) {
+    UnitW wu[S][PU], wg[GATED ? S : 1][PU];
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int m = 0; m < kPartUnits; ++m) {
+      for (int m = 0; m < PU; ++m) {
         const int u = c0[s] + p + lane + kWave * m;
         const bool v = ok[s] && u < c1[s];
         wu[s][m] = load_unit<WF>(w_up, scale_off, rows[s], u, d, v);
@@ -169,7 +173,7 @@ __device__ __forceinline__ void part_dots(const void* w_up, const void* w_gate, 
 #pragma unroll
         for (int s = 0; s < S; ++s)
 #pragma unroll
-          for (int m = 0; m < kPartUnits; ++m) {
+          for (int m = 0; m < PU; ++m) {
             const int u = c0[s] + p + lane + kWave * m;
             if (ok[s] && u < c1[s]) {
               au[s][j] = unit_dot<WF, XL>(wu[s][m], u, xr, xl, au[s][j]);
