@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   }
   u32x4 w0[kPUSub][kP2Chunks];
   issue_pass<W, kPUSub>(p2, rows, rv, rank, g, 0, w0);
-  stage_t(t, t_lds, nt, rank);
+  stage_t<W>(t, t_lds, nt, rank);
   if (XL) stage_x<W>(xb, x_lds, nt, d);
   __syncthreads();
   float acc[kPUSub][NT];

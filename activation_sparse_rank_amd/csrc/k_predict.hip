@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kP2Threads) void k_pred2(const W* __restrict__ p2, 
   // The first step's p2 loads go out before t is staged.
   u32x4 w0[1][kP2Chunks];
   issue_pass<W, 1>(p2, rows, rv, rank, g, 0, w0);
-  stage_t(t, t_lds, nt, rank);
+  stage_t<W>(t, t_lds, nt, rank);
   __syncthreads();
   while (step < n_steps) {
     float acc[1][NT];

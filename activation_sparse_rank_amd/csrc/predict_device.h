@@ -12,13 +12,19 @@ constexpr int kP2Group = 16;   // lanes that share one row of p2
 constexpr int kP2Chunks = 8;   // 16-byte chunks per lane per pass (128 chunks per row pass)
 constexpr int kP2Pass = kP2Group * kP2Chunks;
 
+// t in LDS.  For fp16 weights a 16-byte chunk of a p2 row meets 8 values of
+// t; storing them as 8 consecutive floats would put the 16 lanes of a group
+// 32 bytes apart (a 4-way LDS bank conflict on every read), so each token's
+// t is stored as two arrays of 4-float quads: the first 4 values of every
+// chunk, then the last 4 (lane reads then cover 256 contiguous bytes).
+// fp32 weights: a chunk meets 4 values; t is stored as it is.
 template <typename W>
-__device__ __forceinline__ float dot_chunk_t(u32x4 w, const float* tv, float acc);
+__device__ __forceinline__ float dot_chunk_t(u32x4 w, const float* t_tok, int ch, int rank, float acc);
 
 template <>
-__device__ __forceinline__ float dot_chunk_t<f16>(u32x4 w, const float* tv, float acc) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(tv);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(tv + 4);
+__device__ __forceinline__ float dot_chunk_t<f16>(u32x4 w, const float* t_tok, int ch, int rank, float acc) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(t_tok + ch * 4);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(t_tok + rank / 2 + ch * 4);
   const f16x2 h0 = as_h2(w.x), h1 = as_h2(w.y), h2 = as_h2(w.z), h3 = as_h2(w.w);
   acc = __builtin_fmaf((float)h0.x, a.x, acc);
   acc = __builtin_fmaf((float)h0.y, a.y, acc);
@@ -32,8 +38,8 @@ __device__ __forceinline__ float dot_chunk_t<f16>(u32x4 w, const float* tv, floa
 }
 
 template <>
-__device__ __forceinline__ float dot_chunk_t<float>(u32x4 w, const float* tv, float acc) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(tv);
+__device__ __forceinline__ float dot_chunk_t<float>(u32x4 w, const float* t_tok, int ch, int, float acc) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(t_tok + ch * 4);
   acc = __builtin_fmaf(as_f(w.x), a.x, acc);
   acc = __builtin_fmaf(as_f(w.y), a.y, acc);
   acc = __builtin_fmaf(as_f(w.z), a.z, acc);
@@ -41,11 +47,20 @@ __device__ __forceinline__ float dot_chunk_t<float>(u32x4 w, const float* tv, fl
   return acc;
 }
 
-// Copy the token tile of t ([nt][rank] fp32) into LDS.  rank % 8 == 0.
+// Copy the token tile of t ([nt][rank] fp32) into LDS in the layout above.
+// rank % 8 == 0.
+template <typename W>
 __device__ __forceinline__ void stage_t(const float* __restrict__ t, float* t_lds, int nt, int rank) {
-  const int tot4 = nt * rank / 4;
-  for (int e = threadIdx.x; e < tot4; e += blockDim.x)
-    reinterpret_cast<f32x4*>(t_lds)[e] = reinterpret_cast<const f32x4*>(t)[e];
+  const int q_tok = rank / 4;                     // 16-byte quads per token
+  const int tot4 = nt * q_tok;
+  for (int e = threadIdx.x; e < tot4; e += blockDim.x) {
+    int dst = e;
+    if (sizeof(W) == 2) {
+      const int j = e / q_tok, q = e - j * q_tok;   // quad q = chunk q/2, half q%2
+      dst = j * q_tok + (q & 1) * (q_tok / 2) + (q >> 1);
+    }
+    reinterpret_cast<f32x4*>(t_lds)[dst] = reinterpret_cast<const f32x4*>(t)[e];
+  }
 }
 
 // Logits of S rows per 16-lane group: acc[s][j] = p2[rows[s]] . t[j].
@@ -84,7 +99,7 @@ __device__ __forceinline__ void consume_pass(const u32x4 (&w)[S][kP2Chunks], int
       if (ch < nch) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-          if (j < nt) acc[s][j] = dot_chunk_t<W>(w[s][m], t_lds + j * rank + ch * E, acc[s][j]);
+          if (j < nt) acc[s][j] = dot_chunk_t<W>(w[s][m], t_lds + j * rank, ch, rank, acc[s][j]);
       }
     }
   }
