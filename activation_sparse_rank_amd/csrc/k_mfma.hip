@@ -95,9 +95,15 @@ __device__ __forceinline__ int clamp_count(const int32_t* count_ptr, int max_cou
 // The 4 waves of a workgroup hold accumulators for the same NQ output quads
 // (16x16 blocks, 4 values per lane); sum them in wave order through LDS
 // (red: [4][NQ][4][64] floats).  Thread T gets lane position T%64 of quads
-// q = T/64 + 4e, e < NQ/4, in out[e][0..3].
+// q = T/64 + 4e, e < quads_per_thread(NQ), in out[e][0..3] (with NQ < 4 only
+// the threads with T/64 < NQ own one).
 template <int NQ>
-__device__ __forceinline__ void sum_waves(float* red, const f32x4 (&acc)[NQ], float (&out)[NQ / 4][4]) {
+constexpr int quads_per_thread() { return NQ >= 4 ? NQ / 4 : 1; }
+
+template <int NQ>
+__device__ __forceinline__ void sum_waves(float* red, const f32x4 (&acc)[NQ],
+                                          float (&out)[quads_per_thread<NQ>()][4]) {
+  static_assert(NQ < 4 || NQ % 4 == 0, "quads must split evenly over the 4 waves");
   const int lane = lane_id(), wave = wave_id();
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
@@ -106,13 +112,16 @@ __device__ __forceinline__ void sum_waves(float* red, const f32x4 (&acc)[NQ], fl
   __syncthreads();
   const int ol = threadIdx.x & (kWave - 1), oq = threadIdx.x >> 6;
 #pragma unroll
-  for (int e = 0; e < NQ / 4; ++e) {
+  for (int e = 0; e < quads_per_thread<NQ>(); ++e) {
     const int q = oq + 4 * e;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = red[((0 * NQ + q) * 4 + i) * kWave + ol];
+      float v = 0.f;
+      if (q < NQ) {
+        v = red[((0 * NQ + q) * 4 + i) * kWave + ol];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) v += red[((w * NQ + q) * 4 + i) * kWave + ol];
+        for (int w = 1; w < 4; ++w) v += red[((w * NQ + q) * 4 + i) * kWave + ol];
+      }
       out[e][i] = v;
     }
   }
@@ -251,6 +260,12 @@ __global__ __launch_bounds__(256) void k_xstep(const f16* __restrict__ x, int nt
       *reinterpret_cast<const u32x4*>(x + (size_t)t * d + st * kMuK + src_q * 8);
 }
 
+// 16-row blocks per wave in k_mup: enough rows to reuse each activation
+// operand 4 times at 64 tokens, and at few tokens few enough rows per
+// workgroup that a small union list still spreads over every CU.
+template <int NB>
+constexpr int mup_mb() { return NB == 1 ? 1 : (NB == 2 ? 2 : 4); }
+
 template <typename WF, int ACT, int NB>
 __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_up, const void* __restrict__ w_gate,
                                                     size_t scale_off, const float* __restrict__ bias,
@@ -259,28 +274,30 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
                                                     const int32_t* __restrict__ count_ptr, int max_count,
                                                     f16* __restrict__ h, int ldh) {
   constexpr bool GATED = ACT == ACT_REGLU;
-  constexpr int NQ = kMuMB * NB;           // accumulator quads per lane
+  constexpr int MB = mup_mb<NB>();
+  constexpr int NQ = MB * NB;              // accumulator quads per lane
+  constexpr int QT = quads_per_thread<NQ>();
   __shared__ float red[kMuWaves][NQ][4][kWave];
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
   const int cnt = clamp_count(count_ptr, max_count);
-  const int r0 = blockIdx.x * kMuRows;
+  const int r0 = blockIdx.x * 16 * MB;
   if (r0 >= cnt) return;                   // the whole workgroup leaves together
 
-  int row[kMuMB];
-  bool rv[kMuMB];
+  int row[MB];
+  bool rv[MB];
 #pragma unroll
-  for (int mb = 0; mb < kMuMB; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int p = r0 + mb * 16 + n16;
     const int i = p < cnt ? idx[p] : -1;
     rv[mb] = (unsigned)i < (unsigned)d_ff;
     row[mb] = rv[mb] ? i : 0;
   }
 
-  f32x4 au[kMuMB][NB], ag[GATED ? kMuMB : 1][NB];
+  f32x4 au[MB][NB], ag[GATED ? MB : 1][NB];
 #pragma unroll
-  for (int mb = 0; mb < kMuMB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       au[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -290,8 +307,8 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   const int ns = d / kMuK;
   const int s0 = wave * ns / kMuWaves, s1 = (wave + 1) * ns / kMuWaves;
   struct Step {
-    RowStep<WF, kMuMB> up;
-    RowStep<WF, GATED ? kMuMB : 1> gate;
+    RowStep<WF, MB> up;
+    RowStep<WF, GATED ? MB : 1> gate;
     TokStep<NB> x;
   };
   auto load = [&](Step& S, int st) {
@@ -302,7 +319,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   };
   auto mul = [&](const Step& S) {
 #pragma unroll
-    for (int mb = 0; mb < kMuMB; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       u32x4 a[4], ga[4];
       S.up.operands(mb, a);
       if constexpr (GATED) S.gate.operands(mb, ga);
@@ -330,11 +347,11 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   }
 
   // Sum the 4 waves in wave order.  Thread T owns lane position T%64 and the
-  // quads q = T/64 + 4*e (e < NB): rows 4*((T%64)/16)+i of block q/NB, token
+  // quads q = T/64 + 4*e (e < QT): rows 4*((T%64)/16)+i of block q/NB, token
   // (q%NB)*16 + T%16.
   const int ol = threadIdx.x & (kWave - 1);
   const int oq = threadIdx.x >> 6;
-  float su[NB][4], sg[NB][4];
+  float su[QT][4], sg[QT][4];
   {
     f32x4 flat[NQ];
     if constexpr (GATED) {
@@ -348,12 +365,12 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   }
 
 #pragma unroll
-  for (int e = 0; e < NB; ++e) {
+  for (int e = 0; e < QT; ++e) {
     const int q = oq + kMuWaves * e;
     const int mb = q / NB, nb = q % NB;
     const int t = nb * 16 + (ol & 15);
     const int p = r0 + mb * 16 + 4 * (ol >> 4);
-    if (t < nt) {
+    if (q < NQ && t < nt) {
       f16 hv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
     wr.load(w_dt, scale_off, d, rows, ok, col);
     u32x4 a[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) a[nb] = ld16(h + (size_t)(nb * 16 + n16) * ldh + p0);
+    for (int nb = 0; nb < NB; ++nb) a[nb] = p0 < cnt ? ld16(h + (size_t)(nb * 16 + n16) * ldh + p0) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int q = 0; q < CPL / 8; ++q) {
       u32x4 rw[8], bt[8];
@@ -722,7 +739,8 @@ size_t h_region(int d_ff, int nb) { return up256((size_t)16 * nb * ldh_of(d_ff) 
 
 template <typename WF, int ACT, int NB>
 hipError_t launch_mup(const SparseArgs& a, const f16* x, int nt, f16* h, int ldh, hipStream_t s) {
-  const int grid = (a.max_count + kMuRows - 1) / kMuRows;
+  const int rows_per_wg = 16 * mup_mb<NB>();
+  const int grid = (a.max_count + rows_per_wg - 1) / rows_per_wg;
   if (grid == 0) return hipSuccess;
   const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
   const size_t so = std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
