@@ -124,7 +124,7 @@ hipError_t predict_any(const pi_predictor* pred, const void* x, int n_tok, float
                        const Layout& L, uint8_t* mask, float* logits, hipStream_t s) {
   if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok))
     return pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
-                                   theta, t, ws + L.tpart, mask, logits, s);
+                                   theta, t, ws + L.tpart, mask, logits, nullptr, s);
   hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, nullptr,
                                            0, s);
   if (e != hipSuccess) return e;
@@ -263,9 +263,17 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
     return PI_OK;
   }
   // Many tokens: predict every token, take the union list, then the list path.
-  e = predict_any(pred, x, n_tok, theta_of(tau), t, w, L, mask, nullptr, s);
-  if (e != hipSuccess) return hip_fail(e);
-  e = pi::launch_compact(mask, n_tok, ffn->d_ff, idx, count, s);
+  if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok)) {
+    // the matrix-core predictor writes the union mask directly
+    e = pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
+                                theta_of(tau), t, w + L.tpart, nullptr, nullptr, mask, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = pi::launch_compact(mask, 1, ffn->d_ff, idx, count, s);
+  } else {
+    e = predict_any(pred, x, n_tok, theta_of(tau), t, w, L, mask, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = pi::launch_compact(mask, n_tok, ffn->d_ff, idx, count, s);
+  }
   if (e != hipSuccess) return hip_fail(e);
   e = pi::launch_sparse_ffn(a, s);
   if (e != hipSuccess) return hip_fail(e);

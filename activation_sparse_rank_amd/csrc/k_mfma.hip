@@ -549,7 +549,8 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
 //               the 4 waves);
 //   k_tsplit -- t = the splits added in order (fp32), and t_hi = fp16(t),
 //               t_lo = fp16(t - t_hi);
-//   k_mp2    -- l[j][i] = p2[i] . t[j] + c[i]; mask = l > theta.  t is fp32,
+//   k_mp2    -- l[j][i] = p2[i] . t[j] + c[i]; mask = l > theta (per token,
+//               and optionally the union over the tokens).  t is fp32,
 //               so both t_hi and t_lo are multiplied (products exact in fp32;
 //               t_hi + t_lo carries 22 significant bits).  Needs |t| < 65504.
 // ---------------------------------------------------------------------------
@@ -638,9 +639,12 @@ template <int NB>
 __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, const float* __restrict__ c,
                                                     const f16* __restrict__ th, const f16* __restrict__ tl, int rank,
                                                     int d_ff, int nt, float theta, uint8_t* __restrict__ mask,
-                                                    float* __restrict__ logits) {
+                                                    float* __restrict__ logits, uint8_t* __restrict__ umask,
+                                                    int umask_first) {
   constexpr int NQ = kMuMB * NB;
   __shared__ float red[kMuWaves][NQ][4][kWave];
+  __shared__ int uni[kMuRows];                 // union over the tile's tokens
+  if (threadIdx.x < kMuRows) uni[threadIdx.x] = 0;
   const int lane = lane_id(), wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
   const int r0 = blockIdx.x * kMuRows;
@@ -702,11 +706,18 @@ __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, 
       for (int i = 0; i < 4; ++i) {
         if (r + i < d_ff) {
           const float l = sum[e][i] + c[r + i];
-          mask[(size_t)j * d_ff + r + i] = l > theta ? 1 : 0;
+          if (mask) mask[(size_t)j * d_ff + r + i] = l > theta ? 1 : 0;
           if (logits) logits[(size_t)j * d_ff + r + i] = l;
+          if (l > theta) uni[r + i - r0] = 1;    // every writer stores the same value
         }
       }
     }
+  }
+  if (umask) {
+    __syncthreads();
+    const int i = threadIdx.x;
+    if (i < kMuRows && r0 + i < d_ff)
+      umask[r0 + i] = (uint8_t)(uni[i] | (umask_first ? 0 : umask[r0 + i]));
   }
 }
 
@@ -806,7 +817,8 @@ hipError_t run_mall(const SparseArgs& a, hipStream_t s) {
 
 template <int NB>
 hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x, int nt, int d, int rank, int d_ff,
-                     float theta, float* t, char* ws, uint8_t* mask, float* logits, hipStream_t s) {
+                     float theta, float* t, char* ws, uint8_t* mask, float* logits, uint8_t* umask, int first,
+                     hipStream_t s) {
   const int splits = pred_splits(d);
   float* part = reinterpret_cast<float*>(ws);
   f16* th = reinterpret_cast<f16*>(ws + up256((size_t)splits * kMfmaTile * rank * sizeof(float)));
@@ -825,7 +837,7 @@ hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_mp2<NB>), dim3((d_ff + kMuRows - 1) / kMuRows), dim3(kMuThreads), 0, s, p2, c, th, tl, rank,
-                     d_ff, nt, theta, mask, logits);
+                     d_ff, nt, theta, mask, logits, umask, first);
   return hipGetLastError();
 }
 
@@ -868,25 +880,26 @@ size_t pred_mfma_part_bytes(int d, int rank, int) {
 
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
-                               hipStream_t s) {
+                               uint8_t* umask, hipStream_t s) {
   for (int t0 = 0; t0 < n_tok; t0 += kMfmaTile) {
     const int nt = n_tok - t0 < kMfmaTile ? n_tok - t0 : kMfmaTile;
     const f16* xt = static_cast<const f16*>(x) + (size_t)t0 * d;
     float* tt = t + (size_t)t0 * rank;
-    uint8_t* mt = mask + (size_t)t0 * d_ff;
+    uint8_t* mt = mask ? mask + (size_t)t0 * d_ff : nullptr;
+    const int first = t0 == 0;
     float* lt = logits ? logits + (size_t)t0 * d_ff : nullptr;
     const f16* a = static_cast<const f16*>(p1);
     const f16* b = static_cast<const f16*>(p2);
     char* wsp = static_cast<char*>(ws);
     hipError_t e;
     if (nt <= 16)
-      e = run_ptile<1>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+      e = run_ptile<1>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
     else if (nt <= 32)
-      e = run_ptile<2>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+      e = run_ptile<2>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
     else if (nt <= 48)
-      e = run_ptile<3>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+      e = run_ptile<3>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
     else
-      e = run_ptile<4>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, s);
+      e = run_ptile<4>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -160,12 +160,13 @@ hipError_t launch_sparse_ffn_mfma(const SparseArgs& a, hipStream_t s);
 // Predictor for many tokens on the matrix cores (fp16 predictor, d and rank
 // multiples of 128, more tokens than one pass of the list path's predictor
 // takes).  t: [n_tok][rank] fp32 out; ws: pred_mfma_part_bytes() of
-// workspace (256-byte aligned); mask/logits as launch_predict_stage2.
+// workspace (256-byte aligned); mask/logits as launch_predict_stage2, either
+// may be NULL; umask (nullable): [d_ff], 1 where any token is active.
 bool pred_mfma_path(int wtype, int d, int rank, int n_tok);
 size_t pred_mfma_part_bytes(int d, int rank, int n_tok);
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
-                               hipStream_t s);
+                               uint8_t* umask, hipStream_t s);
 
 // y = sum over c of part[c][0 .. n), in chunk order (fp32 or fp16 out).
 hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, hipStream_t s);
