@@ -300,6 +300,40 @@ def test_layer_falcon_prompt64():
     _layer_check(dl, n_tok=64, tokens_checked=[0, 17, 63], what="falcon prompt 64")
 
 
+@pytest.mark.parametrize("n_tok", [3, 5, 8, 20, 64, 70, 130])
+@pytest.mark.parametrize("act", ["relu", "reglu"])
+def test_layer_many_tokens(n_tok, act):
+    # pi_layer with fp16 weights past the single-token tile: the matrix-core
+    # predictor (its union mask, OR-ed over token tiles beyond 64 tokens), the
+    # compaction of that one row, then the list path (<= 8 tokens) or the
+    # matrix-core FFN; checked against predict + compact + sparse_ffn and the oracle.
+    d, f, r, tau = 1024, 3000, 128, 0.45
+    g = torch.Generator(device="cuda").manual_seed(17 * n_tok + len(act))
+    p1 = (torch.randn((r, d), generator=g, device="cuda") * 0.05).half()
+    p2 = (torch.randn((f, r), generator=g, device="cuda") * 0.05).half()
+    c = (torch.randn(f, generator=g, device="cuda") * 0.5 - 1.0).float()
+    kw = rand_ffn(d, f, act, torch.float16, seed=n_tok)
+    pred, ffn, hk = pi.Predictor(p1, p2, c), pi.FFN(**kw), host_ffn(kw)
+    x = torch.randn((n_tok, d), generator=g, device="cuda").half()
+    mask = torch.empty((n_tok, f), dtype=torch.uint8, device="cuda")
+    pi.predict(pred, x, tau, mask)
+    idx, cnt = _i32(f), _i32(1)
+    pi.compact(mask, idx, cnt)
+    y_sep = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    pi.sparse_ffn(ffn, x, idx, cnt, y_sep)
+    y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    pi.layer(pred, ffn, x, tau, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_sep), "pi_layer differs from predict + compact + sparse_ffn"
+    ref_l, _ = oracle.predict(host(x), host(p1), host(p2), host(c), tau)
+    check_mask(host(mask), ref_l, tau, f"layer n={n_tok}")
+    c_ = int(cnt.item())
+    ref_idx, ref_c = oracle.compact(host(mask))
+    assert c_ == ref_c and np.array_equal(host(idx)[:c_], ref_idx)
+    assert 0 < c_ < f
+    check_y(host(y), oracle.sparse_ffn(host(x), ref_idx, **hk), TOL["f16"], f"layer n={n_tok} {act}")
+
+
 def test_determinism():
     cfg = workload.get_config("falcon40b")
     dl = DeviceLayer(cfg, layer=2)
