@@ -334,6 +334,28 @@ def test_layer_many_tokens(n_tok, act):
     check_y(host(y), oracle.sparse_ffn(host(x), ref_idx, **hk), TOL["f16"], f"layer n={n_tok} {act}")
 
 
+@pytest.mark.parametrize("n_tok", [1, 2, 9])
+def test_layer_degenerate_threshold(n_tok):
+    # tau -> 0: every neuron is listed and pi_layer equals the dense FFN;
+    # tau -> 1: nothing is listed and y is exactly zero.
+    d, f, r = 512, 1536, 64
+    g = torch.Generator(device="cuda").manual_seed(5 + n_tok)
+    p1 = (torch.randn((r, d), generator=g, device="cuda") * 0.02).half()
+    p2 = (torch.randn((f, r), generator=g, device="cuda") * 0.02).half()
+    c = torch.zeros(f, dtype=torch.float32, device="cuda")
+    kw = rand_ffn(d, f, "relu", torch.float16, seed=40 + n_tok)
+    pred, ffn, hk = pi.Predictor(p1, p2, c), pi.FFN(**kw), host_ffn(kw)
+    x = torch.randn((n_tok, d), generator=g, device="cuda").half()
+    y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    pi.layer(pred, ffn, x, 1e-6, y)                 # theta = ln(1e-6 / (1 - 1e-6)), about -13.8
+    y_dense, _ = oracle.dense_ffn(host(x), **hk)
+    check_y(host(y), y_dense, TOL["f16"], "tau -> 0")
+    y.fill_(float("nan"))
+    pi.layer(pred, ffn, x, 1.0 - 1e-6, y)           # theta about +13.8
+    torch.cuda.synchronize()
+    assert torch.all(y == 0), "tau -> 1: nothing listed, y must be exact zeros"
+
+
 def test_determinism():
     cfg = workload.get_config("falcon40b")
     dl = DeviceLayer(cfg, layer=2)
