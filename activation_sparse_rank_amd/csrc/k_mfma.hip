@@ -722,6 +722,106 @@ __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, 
 }
 
 // ---------------------------------------------------------------------------
+// k_mdown_wide: the down projection for 33-64 tokens.  k_mdown's 4 waves
+// share one column tile and split the chunk, so every 128 columns re-read H
+// from the cache hierarchy (at 64 tokens H is half as many bytes as the
+// weight rows).  Here the 4 waves own 4 column tiles and walk the same list
+// positions: pieces of kMwPiece k-steps of H (and of the list) are staged in
+// LDS once per workgroup, and the next step's weight rows are in flight while
+// the current step is multiplied.  Each wave writes its own partial sums.
+// ---------------------------------------------------------------------------
+constexpr int kMwPiece = 16;                 // k-steps (32 list positions each) per staged piece
+
+template <typename WF, int NB, int CPL>
+__global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restrict__ w_dt, size_t scale_off, int d,
+                                                           int d_ff, const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ count_ptr, int max_count,
+                                                           const f16* __restrict__ h, int ldh, int nt, int n_chunks,
+                                                           float* __restrict__ part) {
+  constexpr int HU = kMwPiece * 32 / 8;       // 16-byte units of one token's H in a piece
+  __shared__ u32x4 h_l[16 * NB * HU];
+  __shared__ int rows_l[kMwPiece * 32];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int g = lane >> 4, n16 = lane & 15;
+  const int cnt = clamp_count(count_ptr, max_count);
+  const int ksteps = (cnt + 31) / 32;
+  const int c = blockIdx.y;
+  const int kc0 = (int)((long long)c * ksteps / n_chunks), kc1 = (int)((long long)(c + 1) * ksteps / n_chunks);
+  const int col = (blockIdx.x * kMdWaves + wave) * 16 * CPL + n16 * CPL;
+  const bool cv = col < d;
+
+  f32x4 acc[CPL][NB];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_rows = [&](int q, DownRows<WF, CPL>& wr) {
+    int rows[8];
+    bool ok[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = rows_l[q * 32 + g * 8 + r];
+      ok[r] = cv && i >= 0;
+      rows[r] = ok[r] ? i : 0;
+    }
+    wr.load(w_dt, scale_off, d, rows, ok, col);
+  };
+
+  for (int pb = kc0; pb < kc1; pb += kMwPiece) {
+    const int np = kc1 - pb < kMwPiece ? kc1 - pb : kMwPiece;
+    __syncthreads();                           // the previous piece is no longer read
+    for (int e = threadIdx.x; e < np * 32; e += kMdThreads) {
+      const int p = pb * 32 + e;
+      const int i = p < cnt ? idx[p] : -1;
+      rows_l[e] = (unsigned)i < (unsigned)d_ff ? i : -1;   // past the count or malformed: adds nothing
+    }
+    for (int e = threadIdx.x; e < 16 * NB * np * 4; e += kMdThreads) {
+      const int t = e / (np * 4), u = e - t * (np * 4);
+      const int p = pb * 32 + u * 8;
+      h_l[t * HU + u] = p < cnt ? ld16(h + (size_t)t * ldh + p) : u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    DownRows<WF, CPL> cur, nxt;
+    load_rows(0, cur);
+    for (int q = 0; q < np; ++q) {
+      if (q + 1 < np) load_rows(q + 1, nxt);
+      u32x4 a[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) a[nb] = h_l[(nb * 16 + n16) * HU + q * 4 + g];
+#pragma unroll
+      for (int qq = 0; qq < CPL / 8; ++qq) {
+        u32x4 rw[8], bt[8];
+        cur.group(qq, rw);
+        transpose8x8(rw, bt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[8 * qq + j][nb] = mfma(a[nb], bt[j], acc[8 * qq + j][nb]);
+      }
+      if (q + 1 < np) cur = nxt;
+    }
+  }
+
+  if (cv) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = nb * 16 + 4 * g + i;
+        if (t < nt) {
+          float* dst = part + ((size_t)c * nt + t) * d + col;
+#pragma unroll
+          for (int j = 0; j < CPL; j += 4)
+            *reinterpret_cast<f32x4*>(dst + j) =
+                f32x4{acc[j][nb][i], acc[j + 1][nb][i], acc[j + 2][nb][i], acc[j + 3][nb][i]};
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 constexpr int kMfmaTile = 64;              // tokens per pass
@@ -731,7 +831,9 @@ constexpr int down_cpl(int nb) {
   return std::is_same<WF, Q4>::value ? (nb == 1 ? 32 : (nb == 2 ? 16 : 8)) : 8;
 }
 
-int mfma_chunks(int wtype) { return wtype == 2 ? 16 : 8; }
+// List chunks of the down projection (partial sums per chunk): the wide
+// kernel (33-64 tokens) needs 32 for 2 workgroups per CU.
+int mfma_chunks(int wtype, int nb) { return nb >= 3 ? 32 : (wtype == 2 ? 16 : 8); }
 
 // k splits of the predictor's first product: about 4 steps of 128 per split.
 int pred_splits(int d) {
@@ -783,11 +885,18 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
     e = launch_mup<WF, ACT_RELU, NB>(a, x, nt, h, ldh, s);
   if (e != hipSuccess) return e;
   constexpr int CPL = down_cpl<WF>(NB);
-  const int chunks = mfma_chunks(a.wtype);
+  const int chunks = mfma_chunks(a.wtype, NB);
   const size_t so = std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
-  const dim3 grid((a.d + 16 * CPL - 1) / (16 * CPL), chunks);
-  hipLaunchKernelGGL((k_mdown<WF, NB, CPL>), grid, dim3(kMdThreads), 0, s, a.w_down_t, so, a.d, a.d_ff, a.idx,
-                     a.count, a.max_count, h, ldh, nt, chunks, a.part);
+  if constexpr (NB >= 3) {
+    const int tile = kMdWaves * 16 * CPL;
+    const dim3 grid((a.d + tile - 1) / tile, chunks);
+    hipLaunchKernelGGL((k_mdown_wide<WF, NB, CPL>), grid, dim3(kMdThreads), 0, s, a.w_down_t, so, a.d, a.d_ff, a.idx,
+                       a.count, a.max_count, h, ldh, nt, chunks, a.part);
+  } else {
+    const dim3 grid((a.d + 16 * CPL - 1) / (16 * CPL), chunks);
+    hipLaunchKernelGGL((k_mdown<WF, NB, CPL>), grid, dim3(kMdThreads), 0, s, a.w_down_t, so, a.d, a.d_ff, a.idx,
+                       a.count, a.max_count, h, ldh, nt, chunks, a.part);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t yoff = (size_t)t0 * a.d * (a.ytype == 1 ? 2 : 4);
@@ -854,7 +963,7 @@ void mfma_workspace(int wtype, int d, int d_ff, int n_tok, size_t* h_bytes, size
   const int nb = (nt + 15) / 16;
   (void)nb;
   *h_bytes = h_region(d_ff, 4) + (size_t)kMfmaTile * d * sizeof(f16);
-  *part_bytes = (size_t)mfma_chunks(wtype) * nt * d * sizeof(float);
+  *part_bytes = (size_t)mfma_chunks(wtype, nb) * nt * d * sizeof(float);
 }
 
 hipError_t launch_sparse_ffn_mfma(const SparseArgs& a, hipStream_t s) {
