@@ -820,9 +820,9 @@ int sparse_tile(int wtype, int d) {
 void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices) {
   const int sw = wtype == 2 ? kDqSW : (wtype == 1 ? kWave * 8 : kWave * 4);
   const int slices = (d + sw - 1) / sw;
-  // About 4096 waves (16 per CU) in the fp16/fp32 down kernel (measured: 2%
-  // faster than 2048 at Falcon batch 1; 1024 is 12% slower), 2048 for Q4_0.
-  const int target_wgs = (wtype == 2 ? 2048 : 4096) / kDnWaves;
+  // About 4096 waves (16 per CU) in the down kernel (measured at Falcon
+  // batch 1: 2% faster than 2048 for fp16 and for Q4_0; 1024 is 12% slower).
+  const int target_wgs = 4096 / kDnWaves;
   int c = (target_wgs + slices - 1) / slices;
   if (c < 1) c = 1;
   if (c > 64) c = 64;
