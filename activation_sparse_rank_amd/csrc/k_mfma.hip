@@ -131,6 +131,7 @@ __device__ __forceinline__ void sum_waves(float* red, const f32x4 (&acc)[NQ],
 // ---------------------------------------------------------------------------
 // k_mup
 // ---------------------------------------------------------------------------
+constexpr int kMfmaTokens = 64;           // tokens per pass of the matrix-core path
 constexpr int kMuThreads = 256;
 constexpr int kMuWaves = kMuThreads / kWave;
 constexpr int kMuMB = 4;                   // 16-row blocks per wave (all waves share the rows)
@@ -390,6 +391,161 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
       *reinterpret_cast<u32x2*>(h + (size_t)t * ldh + p) = packed;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// k_mup_wide (33-64 tokens).  k_mup reads the shared activation tile once per
+// 64 rows, and at 64 tokens that tile is as many bytes as the rows: here a
+// workgroup of 8 waves owns 256 list positions and stages pieces of
+// kMxPiece k steps of x in LDS, which all 8 waves multiply.  To keep enough
+// workgroups, k is split over kMxSplit workgroups (grid y) that write fp32
+// partial sums zp[split][token][position] (and zg for the gate); k_mfin adds
+// the splits in order, applies bias and activation and writes H.  (Letting
+// the last workgroup of a row block finish it instead needs device-scope
+// fences, which write back and invalidate the L2 and cost far more.)
+// ---------------------------------------------------------------------------
+constexpr int kMxThreads = 512;
+constexpr int kMxWaves = kMxThreads / kWave;
+constexpr int kMxMB = 2;                          // 16-row blocks per wave
+constexpr int kMxRows = kMxWaves * 16 * kMxMB;    // 256 list positions per workgroup
+constexpr int kMxSplit = 2;
+constexpr int kMxPiece = 8;                       // k steps per staged piece of x
+
+template <typename WF, int ACT, int NB>
+__global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict__ w_up, const void* __restrict__ w_gate,
+                                                         size_t scale_off, const f16* __restrict__ xs, int d,
+                                                         int d_ff, int nt, const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ count_ptr, int max_count,
+                                                         float* __restrict__ zp, float* __restrict__ zg, int ldz) {
+  constexpr bool GATED = ACT == ACT_REGLU;
+  constexpr int XU = 16 * NB * kMuK / 8;          // 16-byte units of one step of x (all token slots)
+  __shared__ u32x4 x_l[kMxPiece][XU];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int g = lane >> 4, n16 = lane & 15;
+  const int cnt = clamp_count(count_ptr, max_count);
+  if (blockIdx.x * kMxRows >= cnt) return;        // the whole workgroup leaves together
+  const int r0 = blockIdx.x * kMxRows + wave * 16 * kMxMB;
+  int row[kMxMB];
+  bool rv[kMxMB];
+#pragma unroll
+  for (int mb = 0; mb < kMxMB; ++mb) {
+    const int p = r0 + mb * 16 + n16;
+    const int i = p < cnt ? idx[p] : -1;
+    rv[mb] = (unsigned)i < (unsigned)d_ff;
+    row[mb] = rv[mb] ? i : 0;
+  }
+  f32x4 au[kMxMB][NB], ag[GATED ? kMxMB : 1][NB];
+#pragma unroll
+  for (int mb = 0; mb < kMxMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      au[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (GATED) ag[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  const int ns = d / kMuK;
+  const int split = blockIdx.y;
+  const int s0 = split * ns / kMxSplit, s1 = (split + 1) * ns / kMxSplit;
+  struct Step {
+    RowStep<WF, kMxMB> up;
+    RowStep<WF, GATED ? kMxMB : 1> gate;
+  };
+  auto load = [&](Step& S, int st) {
+    S.up.load(w_up, scale_off, row, rv, d, st * kMuK, g);
+    if constexpr (GATED) S.gate.load(w_gate, scale_off, row, rv, d, st * kMuK, g);
+  };
+  for (int p0 = s0; p0 < s1; p0 += kMxPiece) {
+    const int np = s1 - p0 < kMxPiece ? s1 - p0 : kMxPiece;
+    Step cur;
+    load(cur, p0);                                  // the first step's rows go out before the staging
+    __syncthreads();                                // the previous piece is no longer read
+    const int su = nt * (kMuK / 8);                 // units of one step of the nt real tokens
+    for (int e = threadIdx.x; e < np * XU; e += kMxThreads) {
+      const int q = e / XU, r = e - q * XU;         // token slots past nt hold zeros
+      x_l[q][r] = r < su ? ld16(xs + ((size_t)(p0 + q) * nt) * kMuK + (size_t)r * 8) : u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    for (int q = 0; q < np; ++q) {
+      Step nxt;
+      if (q + 1 < np) load(nxt, p0 + q + 1);
+      u32x4 a[kMxMB][4], ga[GATED ? kMxMB : 1][4];
+#pragma unroll
+      for (int mb = 0; mb < kMxMB; ++mb) {
+        cur.up.operands(mb, a[mb]);
+        if constexpr (GATED) cur.gate.operands(mb, ga[mb]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 b[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) b[nb] = x_l[q][(nb * 16 + n16) * (kMuK / 8) + 4 * s + g];
+#pragma unroll
+        for (int mb = 0; mb < kMxMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            au[mb][nb] = mfma(a[mb][s], b[nb], au[mb][nb]);
+            if constexpr (GATED) ag[mb][nb] = mfma(ga[mb][s], b[nb], ag[mb][nb]);
+          }
+      }
+      if (q + 1 < np) cur = nxt;
+    }
+  }
+  // partial sums: lane holds rows 4g..4g+3 of each 16-row block, token n16 of each token block
+#pragma unroll
+  for (int mb = 0; mb < kMxMB; ++mb) {
+    const int p = r0 + mb * 16 + 4 * g;
+    if (p < cnt) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int t = nb * 16 + n16;
+        if (t < nt) {
+          *reinterpret_cast<f32x4*>(zp + ((size_t)split * kMfmaTokens + t) * ldz + p) = au[mb][nb];
+          if constexpr (GATED)
+            *reinterpret_cast<f32x4*>(zg + ((size_t)split * kMfmaTokens + t) * ldz + p) = ag[mb][nb];
+        }
+      }
+    }
+  }
+}
+
+// k_mfin: H[t][p] = act(sum of the splits in split order + bias) for
+// p < count, 0 from the count up to the next multiple of 64, fp16.  Each
+// thread does 4 consecutive positions of one token.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_mfin(const float* __restrict__ zp, const float* __restrict__ zg,
+                                              const float* __restrict__ bias, const int32_t* __restrict__ idx,
+                                              const int32_t* __restrict__ count_ptr, int max_count, int d_ff, int nt,
+                                              int ldz, f16* __restrict__ h, int ldh) {
+  constexpr bool GATED = ACT == ACT_REGLU;
+  const int cnt = clamp_count(count_ptr, max_count);
+  const int quads = (cnt + 63) / 64 * 16;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= nt * quads) return;
+  const int t = e / quads, p = (e - t * quads) * 4;
+  f32x4 u{0.f, 0.f, 0.f, 0.f}, gs{0.f, 0.f, 0.f, 0.f};
+  if (p < cnt) {
+#pragma unroll
+    for (int sp = 0; sp < kMxSplit; ++sp) {
+      const size_t o = ((size_t)sp * kMfmaTokens + t) * ldz + p;
+      u += *reinterpret_cast<const f32x4*>(zp + o);
+      if constexpr (GATED) gs += *reinterpret_cast<const f32x4*>(zg + o);
+    }
+  }
+  f16 hv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = p + i < cnt ? idx[p + i] : -1;
+    float v = 0.f;
+    if ((unsigned)n < (unsigned)d_ff) {
+      const float b = bias ? bias[n] : 0.f;
+      v = GATED ? act_fn<ACT>(u[i], gs[i] + b) : act_fn<ACT>(u[i] + b, 0.f);
+    }
+    hv[i] = (f16)v;
+  }
+  u32x2 packed;
+  packed.x = __builtin_bit_cast(unsigned, f16x2{hv[0], hv[1]});
+  packed.y = __builtin_bit_cast(unsigned, f16x2{hv[2], hv[3]});
+  *reinterpret_cast<u32x2*>(h + (size_t)t * ldh + p) = packed;
 }
 
 // ---------------------------------------------------------------------------
@@ -824,7 +980,7 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-constexpr int kMfmaTile = 64;              // tokens per pass
+constexpr int kMfmaTile = kMfmaTokens;
 
 template <typename WF>
 constexpr int down_cpl(int nb) {
@@ -847,11 +1003,41 @@ int ldh_of(int d_ff) { return (d_ff + kMuRows - 1) / kMuRows * kMuRows; }
 size_t up256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Sparse FFN workspace of one token tile: H [64][ldh] fp16, then the
-// step-major activations [d/128][nt][128] fp16.
+// step-major activations [d/128][nt][128] fp16, then (33-64 tokens) the
+// up projection's split partial sums, up and gate, [kMxSplit][64][ldz] fp32.
 size_t h_region(int d_ff, int nb) { return up256((size_t)16 * nb * ldh_of(d_ff) * sizeof(f16)); }
+int ldz_of(int d_ff) { return ldh_of(d_ff); }
+size_t zp_region(int d_ff) { return up256((size_t)kMxSplit * kMfmaTokens * ldz_of(d_ff) * sizeof(float)); }
+size_t wide_region(int d_ff) { return 2 * zp_region(d_ff); }
+size_t xs_region(int d) { return up256((size_t)kMfmaTile * d * sizeof(f16)); }
+
+struct WideWs {
+  float* zp;
+  float* zg;
+};
+WideWs wide_ws(const SparseArgs& a) {
+  char* base = reinterpret_cast<char*>(a.h) + h_region(a.d_ff, 4) + xs_region(a.d);
+  return {reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + zp_region(a.d_ff))};
+}
 
 template <typename WF, int ACT, int NB>
 hipError_t launch_mup(const SparseArgs& a, const f16* x, int nt, f16* h, int ldh, hipStream_t s) {
+  if constexpr (NB >= 3) {
+    const int grid = (a.max_count + kMxRows - 1) / kMxRows;
+    if (grid == 0) return hipSuccess;
+    const size_t so = std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
+    const WideWs w = wide_ws(a);
+    const int ldz = ldz_of(a.d_ff);
+    hipLaunchKernelGGL((k_mup_wide<WF, ACT, NB>), dim3(grid, kMxSplit), dim3(kMxThreads), 0, s, a.w_up, a.w_gate, so,
+                       x, a.d, a.d_ff, nt, a.idx, a.count, a.max_count, w.zp, w.zg, ldz);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
+    const int n = nt * (grid * kMxRows / 4);       // covers nt x (count rounded up to 64) / 4
+    hipLaunchKernelGGL((k_mfin<ACT>), dim3((n + 255) / 256), dim3(256), 0, s, w.zp, w.zg, bias, a.idx, a.count,
+                       a.max_count, a.d_ff, nt, ldz, h, ldh);
+    return hipGetLastError();
+  }
   const int rows_per_wg = 16 * mup_mb<NB>();
   const int grid = (a.max_count + rows_per_wg - 1) / rows_per_wg;
   if (grid == 0) return hipSuccess;
@@ -962,7 +1148,7 @@ void mfma_workspace(int wtype, int d, int d_ff, int n_tok, size_t* h_bytes, size
   const int nt = n_tok < kMfmaTile ? n_tok : kMfmaTile;
   const int nb = (nt + 15) / 16;
   (void)nb;
-  *h_bytes = h_region(d_ff, 4) + (size_t)kMfmaTile * d * sizeof(f16);
+  *h_bytes = h_region(d_ff, 4) + xs_region(d) + (nb >= 3 ? wide_region(d_ff) : 0);
   *part_bytes = (size_t)mfma_chunks(wtype, nb) * nt * d * sizeof(float);
 }
 

@@ -187,7 +187,8 @@ def _ffn_kernels(cfg, n_tok):
     """Kernels of one pi_sparse_ffn call (labels only)."""
     q4 = cfg.wtype == "q4_0"
     if n_tok > _tile(cfg) and cfg.wtype in ("f16", "q4_0") and cfg.d_model % 128 == 0:
-        return f"k_xstep + k_mup + {'k_mdown_wide' if min(n_tok, 64) > 32 else 'k_mdown'} + k_merge"
+        wide = min(n_tok, 64) > 32
+        return f"k_xstep + {'k_mup_wide + k_mfin + k_mdown_wide' if wide else 'k_mup + k_mdown'} + k_merge"
     return f"k_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
 
 
