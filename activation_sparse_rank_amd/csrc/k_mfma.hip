@@ -404,6 +404,10 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
 // the last workgroup of a row block finish it instead needs device-scope
 // fences, which write back and invalidate the L2 and cost far more.)
 // ---------------------------------------------------------------------------
+// One token's 128 k values are 16 units of 16 bytes; LDS copies give each
+// token 17 units, so the 16 tokens of an MFMA operand read fall on
+// different banks (with 16 units they would all hit the same ones).
+constexpr int kTokStride = kMuK / 8 + 1;
 constexpr int kMxThreads = 512;
 constexpr int kMxWaves = kMxThreads / kWave;
 constexpr int kMxMB = 2;                          // 16-row blocks per wave
@@ -418,8 +422,8 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
                                                          const int32_t* __restrict__ count_ptr, int max_count,
                                                          float* __restrict__ zp, float* __restrict__ zg, int ldz) {
   constexpr bool GATED = ACT == ACT_REGLU;
-  constexpr int XU = 16 * NB * kMuK / 8;          // 16-byte units of one step of x (all token slots)
-  __shared__ u32x4 x_l[kMxPiece][XU];
+  constexpr int LU = 16 * NB * kMuK / 8;          // 16-byte units of one step of x (all token slots)
+  __shared__ u32x4 x_l[kMxPiece][16 * NB * kTokStride];
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -460,9 +464,10 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
     load(cur, p0);                                  // the first step's rows go out before the staging
     __syncthreads();                                // the previous piece is no longer read
     const int su = nt * (kMuK / 8);                 // units of one step of the nt real tokens
-    for (int e = threadIdx.x; e < np * XU; e += kMxThreads) {
-      const int q = e / XU, r = e - q * XU;         // token slots past nt hold zeros
-      x_l[q][r] = r < su ? ld16(xs + ((size_t)(p0 + q) * nt) * kMuK + (size_t)r * 8) : u32x4{0, 0, 0, 0};
+    for (int e = threadIdx.x; e < np * LU; e += kMxThreads) {
+      const int q = e / LU, r = e - q * LU;         // token slots past nt hold zeros
+      x_l[q][(r >> 4) * kTokStride + (r & 15)] =
+          r < su ? ld16(xs + ((size_t)(p0 + q) * nt) * kMuK + (size_t)r * 8) : u32x4{0, 0, 0, 0};
     }
     __syncthreads();
     for (int q = 0; q < np; ++q) {
@@ -478,7 +483,7 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
       for (int s = 0; s < 4; ++s) {
         u32x4 b[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) b[nb] = x_l[q][(nb * 16 + n16) * (kMuK / 8) + 4 * s + g];
+        for (int nb = 0; nb < NB; ++nb) b[nb] = x_l[q][(nb * 16 + n16) * kTokStride + 4 * s + g];
 #pragma unroll
         for (int mb = 0; mb < kMxMB; ++mb)
 #pragma unroll
@@ -895,7 +900,8 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
                                                            const f16* __restrict__ h, int ldh, int nt, int n_chunks,
                                                            float* __restrict__ part) {
   constexpr int HU = kMwPiece * 32 / 8;       // 16-byte units of one token's H in a piece
-  __shared__ u32x4 h_l[16 * NB * HU];
+  constexpr int HS = HU + 1;                  // per-token stride in LDS: tokens on different banks
+  __shared__ u32x4 h_l[16 * NB * HS];
   __shared__ int rows_l[kMwPiece * 32];
   const int lane = lane_id();
   const int wave = wave_id();
@@ -936,7 +942,7 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
     for (int e = threadIdx.x; e < 16 * NB * np * 4; e += kMdThreads) {
       const int t = e / (np * 4), u = e - t * (np * 4);
       const int p = pb * 32 + u * 8;
-      h_l[t * HU + u] = p < cnt ? ld16(h + (size_t)t * ldh + p) : u32x4{0, 0, 0, 0};
+      h_l[t * HS + u] = p < cnt ? ld16(h + (size_t)t * ldh + p) : u32x4{0, 0, 0, 0};
     }
     __syncthreads();
     DownRows<WF, CPL> cur, nxt;
@@ -945,7 +951,7 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
       if (q + 1 < np) load_rows(q + 1, nxt);
       u32x4 a[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) a[nb] = h_l[(nb * 16 + n16) * HU + q * 4 + g];
+      for (int nb = 0; nb < NB; ++nb) a[nb] = h_l[(nb * 16 + n16) * HS + q * 4 + g];
 #pragma unroll
       for (int qq = 0; qq < CPL / 8; ++qq) {
         u32x4 rw[8], bt[8];
@@ -974,6 +980,101 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
                 f32x4{acc[j][nb][i], acc[j + 1][nb][i], acc[j + 2][nb][i], acc[j + 3][nb][i]};
         }
       }
+  }
+}
+
+// k_mp2_wide (33-64 tokens): the second product with t_hi and t_lo staged in
+// LDS.  k_mp2 re-reads both from the cache for every 64 rows, as many bytes
+// as the p2 rows themselves at 64 tokens.  Here a workgroup of 8 waves owns
+// 128 rows (16 per wave), walks all of k itself (one accumulator per token
+// block, no cross-wave sum), and stages kMpPiece k steps of t_hi and t_lo
+// per piece; each wave keeps the next step's p2 rows in flight (a whole
+// piece in flight was slower: the staging loads then queue behind it).
+constexpr int kMpThreads = 512;
+constexpr int kMpRows = kMpThreads / kWave * 16;
+constexpr int kMpPiece = 4;
+
+template <int NB>
+__global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__ p2, const float* __restrict__ c,
+                                                         const f16* __restrict__ th, const f16* __restrict__ tl,
+                                                         int rank, int d_ff, int nt, float theta,
+                                                         uint8_t* __restrict__ mask, float* __restrict__ logits,
+                                                         uint8_t* __restrict__ umask, int umask_first) {
+  constexpr int LU = 16 * NB * kMuK / 8;          // 16-byte units of one step (all token slots)
+  __shared__ u32x4 th_l[kMpPiece][16 * NB * kTokStride], tl_l[kMpPiece][16 * NB * kTokStride];
+  __shared__ int uni[kMpRows];                    // union over the tile's tokens
+  if (threadIdx.x < kMpRows) uni[threadIdx.x] = 0;
+  const int lane = lane_id(), wave = wave_id();
+  const int g = lane >> 4, n16 = lane & 15;
+  const int base = blockIdx.x * kMpRows;
+  const int r0 = base + wave * 16;
+  int row[1];
+  bool rv[1];
+  row[0] = r0 + n16;
+  rv[0] = row[0] < d_ff;
+  if (!rv[0]) row[0] = 0;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ns = rank / kMuK;
+  const int su = nt * (kMuK / 8);                 // units of one step of the nt real tokens
+  for (int p0 = 0; p0 < ns; p0 += kMpPiece) {
+    const int np = ns - p0 < kMpPiece ? ns - p0 : kMpPiece;
+    RowStep<f16, 1> cur;
+    cur.load(p2, 0, row, rv, rank, p0 * kMuK, g);  // the first step's rows go out before the staging
+    __syncthreads();                                // the previous piece is no longer read
+    for (int e = threadIdx.x; e < np * LU; e += kMpThreads) {
+      const int q = e / LU, r = e - q * LU;         // token slots past nt hold zeros
+      const size_t o = (size_t)(p0 + q) * nt * kMuK + (size_t)r * 8;
+      const int u = (r >> 4) * kTokStride + (r & 15);
+      th_l[q][u] = r < su ? ld16(th + o) : u32x4{0, 0, 0, 0};
+      tl_l[q][u] = r < su ? ld16(tl + o) : u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    for (int q = 0; q < np; ++q) {
+      RowStep<f16, 1> nxt;
+      if (q + 1 < np) nxt.load(p2, 0, row, rv, rank, (p0 + q + 1) * kMuK, g);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 bh[NB], bl[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int u = (nb * 16 + n16) * kTokStride + 4 * s + g;
+          bh[nb] = th_l[q][u];
+          bl[nb] = tl_l[q][u];
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[nb] = mfma(cur.v[0][s], bh[nb], acc[nb]);
+          acc[nb] = mfma(cur.v[0][s], bl[nb], acc[nb]);
+        }
+      }
+      if (q + 1 < np) cur = nxt;
+    }
+  }
+  __syncthreads();                                  // uni[] cleared before any mark
+  // lane holds rows r0 + 4g .. +3 for token nb * 16 + n16
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j = nb * 16 + n16;
+    const int r = r0 + 4 * g;
+    if (j < nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (r + i < d_ff) {
+          const float l = acc[nb][i] + c[r + i];
+          if (mask) mask[(size_t)j * d_ff + r + i] = l > theta ? 1 : 0;
+          if (logits) logits[(size_t)j * d_ff + r + i] = l;
+          if (l > theta) uni[r + i - base] = 1;     // every writer stores the same value
+        }
+      }
+    }
+  }
+  if (umask) {
+    __syncthreads();
+    const int i = threadIdx.x;
+    if (i < kMpRows && base + i < d_ff)
+      umask[base + i] = (uint8_t)(uni[i] | (umask_first ? 0 : umask[base + i]));
   }
 }
 
@@ -1131,8 +1232,12 @@ hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x,
   hipLaunchKernelGGL(k_tsplit, dim3((n + 255) / 256), dim3(256), 0, s, part, splits, nt, rank, t, th, tl);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_mp2<NB>), dim3((d_ff + kMuRows - 1) / kMuRows), dim3(kMuThreads), 0, s, p2, c, th, tl, rank,
-                     d_ff, nt, theta, mask, logits, umask, first);
+  if constexpr (NB >= 3)
+    hipLaunchKernelGGL((k_mp2_wide<NB>), dim3((d_ff + kMpRows - 1) / kMpRows), dim3(kMpThreads), 0, s, p2, c, th, tl,
+                       rank, d_ff, nt, theta, mask, logits, umask, first);
+  else
+    hipLaunchKernelGGL((k_mp2<NB>), dim3((d_ff + kMuRows - 1) / kMuRows), dim3(kMuThreads), 0, s, p2, c, th, tl,
+                       rank, d_ff, nt, theta, mask, logits, umask, first);
   return hipGetLastError();
 }
 
