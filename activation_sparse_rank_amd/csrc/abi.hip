@@ -124,7 +124,8 @@ hipError_t predict_any(const pi_predictor* pred, const void* x, int n_tok, float
                        const Layout& L, uint8_t* mask, float* logits, hipStream_t s) {
   if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok))
     return pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
-                                   theta, t, ws + L.tpart, mask, logits, nullptr, s);
+                                   theta, t, ws + L.tpart, mask, logits, nullptr, nullptr, 0, nullptr, nullptr,
+                                   nullptr, s);
   hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, nullptr,
                                            0, s);
   if (e != hipSuccess) return e;
@@ -264,11 +265,14 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
   }
   // Many tokens: predict every token, take the union list, then the list path.
   if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok)) {
-    // the matrix-core predictor writes the union mask directly
+    // The matrix-core predictor writes the union mask and lists it (idx,
+    // count) in its last kernel; the fp16 FFN reuses its step-major copy
+    // of a single token tile.
+    const void* xs = nullptr;
     e = pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
-                                theta_of(tau), t, w + L.tpart, nullptr, nullptr, mask, s);
-    if (e != hipSuccess) return hip_fail(e);
-    e = pi::launch_compact(mask, 1, ffn->d_ff, idx, count, s);
+                                theta_of(tau), t, w + L.tpart, nullptr, nullptr, mask, status, L.n_segments, idx,
+                                count, &xs, s);
+    a.xs_pre = xs;
   } else {
     e = predict_any(pred, x, n_tok, theta_of(tau), t, w, L, mask, nullptr, s);
     if (e != hipSuccess) return hip_fail(e);

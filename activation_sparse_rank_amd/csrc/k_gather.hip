@@ -282,7 +282,12 @@ constexpr int kPURows = kPUThreads / kP2Group * kPUSub;               // 32 neur
 constexpr int kPULoads = 8;                                           // status loads per thread per batch
 constexpr unsigned kReady = 0x80000000u;
 constexpr int kSpinLimit = 1 << 16;
-constexpr int kPUBatch = 4;                                           // rows per phase-C batch (ReLU)
+// Rows per phase-C batch (ReLU; ReGLU half as many).  A fp16 row part is 64
+// bytes per lane, a Q4_0 row part 18: Q4_0 batches hold 3x as many rows in
+// the same registers, so a segment with many active neurons needs fewer
+// dependent round trips.
+template <typename WF>
+constexpr int pu_batch() { return std::is_same<WF, Q4>::value ? 8 : 4; }
 
 template <typename W, typename WF, int ACT, int NT, bool XL>
 __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2, const float* __restrict__ c,
@@ -345,9 +350,9 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
     __hip_atomic_store(&status[wg], kReady | (unsigned)n_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- C: up projection of the active neurons: wave q computes part q of
-  // every active row, kPUBatch rows at a time with all their loads in flight.
+  // every active row, pu_batch rows at a time with all their loads in flight.
   {
-    constexpr int S = ACT == ACT_REGLU ? kPUBatch / 2 : kPUBatch;
+    constexpr int S = ACT == ACT_REGLU ? pu_batch<WF>() / 2 : pu_batch<WF>();
     unsigned long long bits = am;                  // the same in every wave
     while (bits) {
       int rows[S], parts[S], rr[S];
@@ -657,28 +662,43 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
 
 // ---------------------------------------------------------------------------
 // k_merge: y[j][col] = sum over chunks c = 0, 1, ... of part[c][j][col], in
-// chunk order; one thread per output with up to 32 chunk loads in flight.
+// chunk order.  A workgroup owns 4*QW consecutive outputs, QW = 256 / G with
+// G = n_chunks rounded up to a power of two (at most 64): thread (g, q) loads
+// the 16 bytes of outputs [4q, 4q+4) of chunk g, so every load of the merge
+// is in flight at once and the reads spread over n/(4*QW) workgroups (256 at
+// one Falcon token with 32 chunks).  The sums then run down the chunks in LDS,
+// one output per thread, in chunk order.
 // ---------------------------------------------------------------------------
 constexpr int kMgThreads = 256;
-constexpr int kMgBatch = 32;
+constexpr int kMgMaxChunks = 64;
+
+__host__ __device__ constexpr int merge_group(int n_chunks) {
+  return n_chunks <= 1 ? 1 : (n_chunks <= 2 ? 2 : (n_chunks <= 4 ? 4 : (n_chunks <= 8 ? 8 :
+         (n_chunks <= 16 ? 16 : (n_chunks <= 32 ? 32 : 64)))));
+}
 
 __global__ __launch_bounds__(kMgThreads) void k_merge(const float* __restrict__ part, int n_chunks, int n,
                                                       void* __restrict__ y, int ytype) {
-  const int e = blockIdx.x * kMgThreads + threadIdx.x;
-  if (e >= n) return;
-  float s = 0.f;
-  for (int c0 = 0; c0 < n_chunks; c0 += kMgBatch) {
-    float v[kMgBatch];
-#pragma unroll
-    for (int u = 0; u < kMgBatch; ++u) v[u] = c0 + u < n_chunks ? part[(size_t)(c0 + u) * n + e] : 0.f;
-#pragma unroll
-    for (int u = 0; u < kMgBatch; ++u)
-      if (c0 + u < n_chunks) s += v[u];
+  __shared__ float buf[kMgThreads * 4];
+  const int G = merge_group(n_chunks);
+  const int QW = kMgThreads / G;                 // 16-byte quads per workgroup
+  const int ncol = 4 * QW;
+  const int col0 = blockIdx.x * ncol;
+  const int q = threadIdx.x % QW, g = threadIdx.x / QW;
+  const int col = col0 + 4 * q;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (g < n_chunks && col < n) v = *reinterpret_cast<const float4*>(part + (size_t)g * n + col);
+  reinterpret_cast<float4*>(buf)[threadIdx.x] = v;   // buf[g][4q .. 4q+3]
+  __syncthreads();
+  const int o = threadIdx.x;
+  if (o < ncol && col0 + o < n) {
+    float s = 0.f;
+    for (int c = 0; c < n_chunks; ++c) s += buf[c * ncol + o];
+    if (ytype == 1)
+      static_cast<f16*>(y)[col0 + o] = (f16)s;
+    else
+      static_cast<float*>(y)[col0 + o] = s;
   }
-  if (ytype == 1)
-    static_cast<f16*>(y)[e] = (f16)s;
-  else
-    static_cast<float*>(y)[e] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -834,8 +854,11 @@ int layer_segments(int d_ff) { return (d_ff + kPURows - 1) / kPURows; }
 
 hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_merge, dim3((n + kMgThreads - 1) / kMgThreads), dim3(kMgThreads), 0, s, part, n_chunks, n, y,
-                     ytype);
+  // The merge reads whole 16-byte quads of the partials.
+  if (n_chunks < 1 || n_chunks > kMgMaxChunks || n % 4 != 0 || (reinterpret_cast<uintptr_t>(part) & 15) != 0)
+    return hipErrorInvalidValue;
+  const int ncol = 4 * (kMgThreads / merge_group(n_chunks));
+  hipLaunchKernelGGL(k_merge, dim3((n + ncol - 1) / ncol), dim3(kMgThreads), 0, s, part, n_chunks, n, y, ytype);
   return hipGetLastError();
 }
 

@@ -773,13 +773,73 @@ __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, 
   }
 }
 
+// In-kernel compaction of the union mask (layer path, last token tile of
+// the predictor): the workgroup's R rows are marked 0/1 in uni[] (LDS).  It
+// publishes its marked count as one atomic word that carries its own ready
+// flag, adds the counts of the workgroups before it (dispatched before it, so
+// the grid needs no co-residency), and writes the marked rows' numbers at
+// their list positions in ascending order; the last workgroup writes the
+// count.  The list equals k_compact's over the same union row.  status[] is
+// zero at launch (k_tsplit clears it); every wait is bounded, so the grid
+// always drains.
+// ---------------------------------------------------------------------------
+constexpr unsigned kListReady = 0x80000000u;
+constexpr int kListSpin = 1 << 16;
+
+template <int THREADS, int R>
+__device__ void list_marked(const int* __restrict__ uni, int base, int d_ff, unsigned* __restrict__ status,
+                            int32_t* __restrict__ idx, int32_t* __restrict__ count, int* wl /* [THREADS/64] */) {
+  static_assert(R <= THREADS && R % kWave == 0, "one thread per row");
+  constexpr int W = THREADS / kWave;
+  const int lane = lane_id(), wave = wave_id();
+  const int i = threadIdx.x;
+  const bool mine = i < R && base + i < d_ff && uni[i] != 0;
+  const unsigned long long bm = __ballot(mine);
+  if (lane == 0) wl[wave] = __builtin_popcountll(bm);
+  __syncthreads();
+  int n_g = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const int cw = wl[w];
+    before += w < wave ? cw : 0;
+    n_g += cw;
+  }
+  const int wg = blockIdx.x;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&status[wg], kListReady | (unsigned)n_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int part = 0;
+  for (int p = threadIdx.x; p < wg; p += THREADS) {
+    unsigned v = __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int spin = 0; !(v & kListReady) && spin < kListSpin; ++spin) {
+      __builtin_amdgcn_s_sleep(2);
+      v = __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    part += (int)(v & ~kListReady);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+  __syncthreads();                                  // every wave has read wl[] above
+  if (lane == 0) wl[wave] = part;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) off += wl[w];
+  if (mine) idx[off + before + __builtin_popcountll(bm & ((1ull << lane) - 1ull))] = base + i;
+  if (wg == (int)gridDim.x - 1 && threadIdx.x == 0) *count = off + n_g;
+}
+
+// ---------------------------------------------------------------------------
 // k_tsplit: t = sum of the k splits of the first product in split order
 // (fp32), and its fp16 split t_hi = fp16(t), t_lo = fp16(t - t_hi), stored
 // step-major ([rank/128][nt][128]) for k_mp2.
+// It also clears zero_n words at zero_ptr (the list counters of k_mp2 /
+// k_mp2_wide in the same call); NULL skips it.
 __global__ __launch_bounds__(256) void k_tsplit(const float* __restrict__ part, int n_split, int nt, int rank,
-                                                float* __restrict__ t, f16* __restrict__ th, f16* __restrict__ tl) {
+                                                float* __restrict__ t, f16* __restrict__ th, f16* __restrict__ tl,
+                                                unsigned* __restrict__ zero_ptr, int zero_n) {
   const int n = nt * rank;
   const int e = blockIdx.x * 256 + threadIdx.x;
+  if (zero_ptr != nullptr && e < zero_n) zero_ptr[e] = 0u;
   if (e >= n) return;
   float v[16];
 #pragma unroll
@@ -801,10 +861,12 @@ __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, 
                                                     const f16* __restrict__ th, const f16* __restrict__ tl, int rank,
                                                     int d_ff, int nt, float theta, uint8_t* __restrict__ mask,
                                                     float* __restrict__ logits, uint8_t* __restrict__ umask,
-                                                    int umask_first) {
+                                                    int umask_first, unsigned* __restrict__ status,
+                                                    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
   constexpr int NQ = kMuMB * NB;
   __shared__ float red[kMuWaves][NQ][4][kWave];
   __shared__ int uni[kMuRows];                 // union over the tile's tokens
+  __shared__ int wl[kMuWaves];
   if (threadIdx.x < kMuRows) uni[threadIdx.x] = 0;
   const int lane = lane_id(), wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -877,8 +939,15 @@ __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, 
   if (umask) {
     __syncthreads();
     const int i = threadIdx.x;
-    if (i < kMuRows && r0 + i < d_ff)
-      umask[r0 + i] = (uint8_t)(uni[i] | (umask_first ? 0 : umask[r0 + i]));
+    if (i < kMuRows && r0 + i < d_ff) {
+      const int u = uni[i] | (umask_first ? 0 : umask[r0 + i]);
+      umask[r0 + i] = (uint8_t)u;
+      uni[i] = u;
+    }
+    if (idx) {
+      __syncthreads();
+      list_marked<kMuThreads, kMuRows>(uni, r0, d_ff, status, idx, count, wl);
+    }
   }
 }
 
@@ -999,10 +1068,13 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
                                                          const f16* __restrict__ th, const f16* __restrict__ tl,
                                                          int rank, int d_ff, int nt, float theta,
                                                          uint8_t* __restrict__ mask, float* __restrict__ logits,
-                                                         uint8_t* __restrict__ umask, int umask_first) {
+                                                         uint8_t* __restrict__ umask, int umask_first,
+                                                         unsigned* __restrict__ status, int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ count) {
   constexpr int LU = 16 * NB * kMuK / 8;          // 16-byte units of one step (all token slots)
   __shared__ u32x4 th_l[kMpPiece][16 * NB * kTokStride], tl_l[kMpPiece][16 * NB * kTokStride];
   __shared__ int uni[kMpRows];                    // union over the tile's tokens
+  __shared__ int wl[kMpThreads / kWave];
   if (threadIdx.x < kMpRows) uni[threadIdx.x] = 0;
   const int lane = lane_id(), wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -1073,8 +1145,15 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
   if (umask) {
     __syncthreads();
     const int i = threadIdx.x;
-    if (i < kMpRows && base + i < d_ff)
-      umask[base + i] = (uint8_t)(uni[i] | (umask_first ? 0 : umask[base + i]));
+    if (i < kMpRows && base + i < d_ff) {
+      const int u = uni[i] | (umask_first ? 0 : umask[base + i]);
+      umask[base + i] = (uint8_t)u;
+      uni[i] = u;
+    }
+    if (idx) {
+      __syncthreads();
+      list_marked<kMpThreads, kMpRows>(uni, base, d_ff, status, idx, count, wl);
+    }
   }
 }
 
@@ -1155,7 +1234,9 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
   f16* h = reinterpret_cast<f16*>(a.h);
   const int ldh = ldh_of(a.d_ff);
   hipError_t e;
-  {
+  if (!std::is_same<WF, Q4>::value && a.xs_pre != nullptr && t0 == 0 && nt == a.n_tok) {
+    x = static_cast<const f16*>(a.xs_pre);          // the predictor's step-major copy of the same tile
+  } else {
     f16* xs = reinterpret_cast<f16*>(reinterpret_cast<char*>(a.h) + h_region(a.d_ff, 4));
     const int n_groups = nt * a.d / 8;
     hipLaunchKernelGGL((k_xstep<std::is_same<WF, Q4>::value>), dim3((n_groups + 255) / 256), dim3(256), 0, s, x, nt,
@@ -1211,10 +1292,19 @@ hipError_t run_mall(const SparseArgs& a, hipStream_t s) {
 // Workspace of one predictor token tile: the k-split partials, t_hi, t_lo
 // and the step-major copy of the tokens.
 
+// List (nullable idx): the union mask is also compacted into idx / count in
+// the second product's kernel, which needs at most n_status counters.
+struct PredList {
+  unsigned* status;
+  int n_status;
+  int32_t* idx;
+  int32_t* count;
+};
+
 template <int NB>
 hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x, int nt, int d, int rank, int d_ff,
                      float theta, float* t, char* ws, uint8_t* mask, float* logits, uint8_t* umask, int first,
-                     hipStream_t s) {
+                     const PredList& pl, const f16** xs_out, hipStream_t s) {
   const int splits = pred_splits(d);
   float* part = reinterpret_cast<float*>(ws);
   f16* th = reinterpret_cast<f16*>(ws + up256((size_t)splits * kMfmaTile * rank * sizeof(float)));
@@ -1228,16 +1318,26 @@ hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x,
                      rank, nt, part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (xs_out) *xs_out = xs;
+  const int grid2 = NB >= 3 ? (d_ff + kMpRows - 1) / kMpRows : (d_ff + kMuRows - 1) / kMuRows;
+  const bool list = pl.idx != nullptr && umask != nullptr;
+  if (list && (pl.status == nullptr || pl.count == nullptr || grid2 > pl.n_status)) return hipErrorInvalidValue;
   const int n = nt * rank;
-  hipLaunchKernelGGL(k_tsplit, dim3((n + 255) / 256), dim3(256), 0, s, part, splits, nt, rank, t, th, tl);
+  const int zn = list ? grid2 : 0;
+  const int nz = n > zn ? n : zn;
+  hipLaunchKernelGGL(k_tsplit, dim3((nz + 255) / 256), dim3(256), 0, s, part, splits, nt, rank, t, th, tl,
+                     list ? pl.status : nullptr, zn);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  unsigned* st = list ? pl.status : nullptr;
+  int32_t* li = list ? pl.idx : nullptr;
+  int32_t* lc = list ? pl.count : nullptr;
   if constexpr (NB >= 3)
-    hipLaunchKernelGGL((k_mp2_wide<NB>), dim3((d_ff + kMpRows - 1) / kMpRows), dim3(kMpThreads), 0, s, p2, c, th, tl,
-                       rank, d_ff, nt, theta, mask, logits, umask, first);
+    hipLaunchKernelGGL((k_mp2_wide<NB>), dim3(grid2), dim3(kMpThreads), 0, s, p2, c, th, tl, rank, d_ff, nt, theta,
+                       mask, logits, umask, first, st, li, lc);
   else
-    hipLaunchKernelGGL((k_mp2<NB>), dim3((d_ff + kMuRows - 1) / kMuRows), dim3(kMuThreads), 0, s, p2, c, th, tl,
-                       rank, d_ff, nt, theta, mask, logits, umask, first);
+    hipLaunchKernelGGL((k_mp2<NB>), dim3(grid2), dim3(kMuThreads), 0, s, p2, c, th, tl, rank, d_ff, nt, theta, mask,
+                       logits, umask, first, st, li, lc);
   return hipGetLastError();
 }
 
@@ -1280,9 +1380,14 @@ size_t pred_mfma_part_bytes(int d, int rank, int) {
 
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
-                               uint8_t* umask, hipStream_t s) {
+                               uint8_t* umask, unsigned* status, int n_status, int32_t* idx, int32_t* count,
+                               const void** xs_out, hipStream_t s) {
+  if (xs_out) *xs_out = nullptr;
   for (int t0 = 0; t0 < n_tok; t0 += kMfmaTile) {
     const int nt = n_tok - t0 < kMfmaTile ? n_tok - t0 : kMfmaTile;
+    const bool last = t0 + nt == n_tok;
+    const PredList pl{status, n_status, last ? idx : nullptr, count};
+    const f16* xs = nullptr;
     const f16* xt = static_cast<const f16*>(x) + (size_t)t0 * d;
     float* tt = t + (size_t)t0 * rank;
     uint8_t* mt = mask ? mask + (size_t)t0 * d_ff : nullptr;
@@ -1293,14 +1398,15 @@ hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, c
     char* wsp = static_cast<char*>(ws);
     hipError_t e;
     if (nt <= 16)
-      e = run_ptile<1>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
+      e = run_ptile<1>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
     else if (nt <= 32)
-      e = run_ptile<2>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
+      e = run_ptile<2>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
     else if (nt <= 48)
-      e = run_ptile<3>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
+      e = run_ptile<3>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
     else
-      e = run_ptile<4>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, s);
+      e = run_ptile<4>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
     if (e != hipSuccess) return e;
+    if (xs_out && t0 == 0 && last) *xs_out = xs;     // one tile: its step-major copy stays valid
   }
   return hipSuccess;
 }

@@ -123,6 +123,9 @@ struct SparseArgs {
   float* h;                 // workspace [tile][d_ff] fp32, by list position
   float* part;              // workspace [n_chunks][tile][d] fp32
   int n_chunks, n_slices;
+  // Matrix-core path, fp16 weights, one token tile: x already copied
+  // step-major ([d/128][n_tok][128] fp16) by the predictor; NULL: copy it.
+  const void* xs_pre = nullptr;
 };
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
 
@@ -162,11 +165,15 @@ hipError_t launch_sparse_ffn_mfma(const SparseArgs& a, hipStream_t s);
 // takes).  t: [n_tok][rank] fp32 out; ws: pred_mfma_part_bytes() of
 // workspace (256-byte aligned); mask/logits as launch_predict_stage2, either
 // may be NULL; umask (nullable): [d_ff], 1 where any token is active.
+// With umask and idx given, the union is also listed (ascending) into idx
+// and count, using status[n_status] as counters (cleared in the call).
+// xs_out (nullable) receives the step-major token copy when n_tok <= 64.
 bool pred_mfma_path(int wtype, int d, int rank, int n_tok);
 size_t pred_mfma_part_bytes(int d, int rank, int n_tok);
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
-                               uint8_t* umask, hipStream_t s);
+                               uint8_t* umask, unsigned* status, int n_status, int32_t* idx, int32_t* count,
+                               const void** xs_out, hipStream_t s);
 
 // y = sum over c of part[c][0 .. n), in chunk order (fp32 or fp16 out).
 hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, hipStream_t s);

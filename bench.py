@@ -197,7 +197,14 @@ def _kernels(cfg, n_tok):
     pred = _pred_kernels(cfg, n_tok)
     if n_tok <= _tile(cfg) and n_tok <= 8 and pred == "k_pred1 + k_pred2":
         return f"k_pred1 + k_pred_up + {'k_down_q4' if cfg.wtype == 'q4_0' else 'k_down'} + k_merge"
-    return f"{pred} + k_compact + {_ffn_kernels(cfg, n_tok)}"
+    ffn = _ffn_kernels(cfg, n_tok)
+    if pred.startswith("k_xstep"):
+        # the matrix-core predictor also lists the union; an fp16 FFN over
+        # one token tile reuses the predictor's step-major copy of x
+        if cfg.wtype == "f16" and n_tok <= 64 and ffn.startswith("k_xstep + "):
+            ffn = ffn[len("k_xstep + "):]
+        return f"{pred} (+ list) + {ffn}"
+    return f"{pred} + k_compact + {ffn}"
 
 
 def main(argv=None):
