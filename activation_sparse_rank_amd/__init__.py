@@ -11,7 +11,11 @@ from .api import (  # noqa: F401
     Predictor,
     alloc_workspace,
     compact,
+    count_active,
+    hot_order,
     layer,
+    permute_rows,
+    place_layer,
     predict,
     q4_0_repack,
     sparse_ffn,

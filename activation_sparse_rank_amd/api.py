@@ -221,3 +221,70 @@ def q4_0_repack(src, rows: int, cols: int, dst=None, stream=None):
     st = L.load().pi_q4_0_repack(src.data_ptr(), int(rows), int(cols), dst.data_ptr(), _stream(stream))
     _check(st, "pi_q4_0_repack")
     return dst
+
+
+# ---------------------------------------------------------------------------
+# Neuron placement by hotness (offline, at load time)
+# ---------------------------------------------------------------------------
+
+def count_active(mask, counts, stream=None):
+    """counts[i] += number of tokens whose mask row marks neuron i (pi_count_active)."""
+    _dev(mask, "mask"), _dev(counts, "counts")
+    if mask.dtype != torch.uint8 or mask.dim() != 2:
+        raise ValueError("mask must be uint8 [n_tok, d_ff]")
+    n, f = mask.shape
+    if counts.dtype != torch.int32 or counts.numel() != f:
+        raise ValueError("counts must be int32 [d_ff] (read as uint32)")
+    st = L.load().pi_count_active(mask.data_ptr(), n, f, counts.data_ptr(), _stream(stream))
+    _check(st, "pi_count_active")
+
+
+def hot_order(counts) -> torch.Tensor:
+    """Placement order from firing counts (pi_hot_order, host memory): perm[k]
+    is the neuron placed at row k."""
+    c = counts.detach().to("cpu").contiguous()
+    if c.dtype != torch.int32 or c.dim() != 1:
+        raise ValueError("counts must be int32 [d_ff]")
+    perm = torch.empty(c.numel(), dtype=torch.int32)
+    st = L.load().pi_hot_order(c.data_ptr(), c.numel(), perm.data_ptr())
+    _check(st, "pi_hot_order")
+    return perm
+
+
+def permute_rows(src, perm, dst=None, stream=None):
+    """dst row k = src row perm[k] over the first dimension (pi_permute_rows)."""
+    _dev(src, "src"), _dev(perm, "perm")
+    rows = src.shape[0]
+    if perm.dtype != torch.int32 or perm.numel() != rows:
+        raise ValueError("perm must be int32 with one entry per row of src")
+    row_bytes = src.numel() * src.element_size() // rows
+    if dst is None:
+        dst = torch.empty_like(src)
+    _dev(dst, "dst")
+    if dst.shape != src.shape or dst.dtype != src.dtype:
+        raise ValueError("dst must match src in shape and dtype")
+    st = L.load().pi_permute_rows(src.data_ptr(), rows, row_bytes, perm.data_ptr(), dst.data_ptr(),
+                                  _stream(stream))
+    _check(st, "pi_permute_rows")
+    return dst
+
+
+# Per-neuron arrays of a layer, by the names Predictor / FFN take.
+NEURON_ARRAYS = ("p2", "c", "w_up", "w_gate", "w_down_t", "b_up", "b_gate")
+
+
+def place_layer(tensors: dict, perm) -> dict:
+    """Apply one neuron permutation to every per-neuron array present in
+    tensors (rows of p2, w_up, w_gate, w_down_t -- canonical Q4_0 blocks for
+    Q4_0 weights, before q4_0_repack -- and entries of c, b_up, b_gate);
+    other entries are passed through.  Returns a new dict."""
+    out = dict(tensors)
+    pd = None
+    for k in NEURON_ARRAYS:
+        t = tensors.get(k)
+        if t is None:
+            continue
+        if pd is None or pd.device != t.device:
+            pd = perm.to(device=t.device, dtype=torch.int32).contiguous()
+        out[k] = permute_rows(t, pd)
+    return out

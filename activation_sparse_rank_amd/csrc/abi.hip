@@ -296,6 +296,34 @@ pi_status pi_q4_0_repack(const void* src, int32_t rows, int32_t cols, void* dst,
   return PI_OK;
 }
 
+pi_status pi_count_active(const uint8_t* mask, int32_t n_tok, int32_t d_ff, uint32_t* counts, void* stream) {
+  if (!mask || !counts) return PI_E_NULL;
+  if (n_tok < 1 || d_ff < 1) return PI_E_SHAPE;
+  const hipError_t e = pi::launch_count_active(mask, n_tok, d_ff, counts, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_hot_order(const uint32_t* counts, int32_t d_ff, int32_t* perm) {
+  if (!counts || !perm) return PI_E_NULL;
+  if (d_ff < 1) return PI_E_SHAPE;
+  pi::hot_order(counts, d_ff, PI_SEGMENT_ROWS, perm);
+  return PI_OK;
+}
+
+pi_status pi_permute_rows(const void* src, int32_t rows, int32_t row_bytes, const int32_t* perm, void* dst,
+                          void* stream) {
+  if (!src || !dst || !perm) return PI_E_NULL;
+  if (rows < 1 || row_bytes < 4 || row_bytes % 4) return PI_E_SHAPE;
+  if (!al16(src) || !al16(dst)) return PI_E_ALIGN;
+  const size_t bytes = (size_t)rows * (size_t)row_bytes;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return PI_E_RANGE;   // overlapping buffers
+  const hipError_t e = pi::launch_permute_rows(src, rows, row_bytes, perm, dst, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
 const char* pi_status_str(pi_status s) {
   switch (s) {
     case PI_OK: return "ok";

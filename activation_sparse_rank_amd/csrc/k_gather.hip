@@ -24,6 +24,7 @@
 // All kernels but the merge are bound by HBM bandwidth on the weight rows.
 #include <type_traits>
 
+#include "pi.h"
 #include "predict_device.h"
 
 namespace pi {
@@ -279,6 +280,7 @@ constexpr int kPUThreads = 256;
 constexpr int kPUWaves = kPUThreads / kWave;
 constexpr int kPUSub = 2;                                             // neurons per group
 constexpr int kPURows = kPUThreads / kP2Group * kPUSub;               // 32 neurons per workgroup
+static_assert(kPURows == PI_SEGMENT_ROWS, "the segment size pi_hot_order deals neurons over");
 constexpr int kPULoads = 8;                                           // status loads per thread per batch
 constexpr unsigned kReady = 0x80000000u;
 constexpr int kSpinLimit = 1 << 16;

@@ -180,4 +180,11 @@ hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int yty
 
 hipError_t launch_q4_0_repack(const void* src, int rows, int cols, void* dst, hipStream_t s);
 
+// Neuron placement (k_place.hip): firing counts from masks, the placement
+// order from the counts (host), and a row permutation dst[k] = src[perm[k]].
+hipError_t launch_count_active(const uint8_t* mask, int n_tok, int d_ff, uint32_t* counts, hipStream_t s);
+void hot_order(const uint32_t* counts, int d_ff, int seg, int32_t* perm);
+hipError_t launch_permute_rows(const void* src, int rows, int row_bytes, const int32_t* perm, void* dst,
+                               hipStream_t s);
+
 }  // namespace pi

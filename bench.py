@@ -176,6 +176,22 @@ def _tile(cfg):
     return t
 
 
+def place_by_hotness(pi, cfg, lw, layer, seed, n_cal, dev):
+    """Offline placement of one layer's neurons: run the layer's predictor on
+    n_cal calibration tokens (a token stream of their own, never timed),
+    count each neuron's predicted firings, and permute every per-neuron array
+    into the order pi_hot_order gives (canonical Q4_0 blocks, before the
+    repack)."""
+    import workload
+
+    xc = workload.make_tokens(cfg, layer, n_cal, dev, seed, stream=2)
+    mask = torch.empty((n_cal, cfg.d_ff), dtype=torch.uint8, device=dev)
+    pi.predict(pi.Predictor(lw["p1"], lw["p2"], lw["c"]), xc, cfg.tau, mask)
+    counts = torch.zeros(cfg.d_ff, dtype=torch.int32, device=dev)
+    pi.count_active(mask, counts)
+    return pi.place_layer(lw, pi.hot_order(counts))
+
+
 def _pred_kernels(cfg, n_tok):
     """Kernels of one pi_predict call (labels only)."""
     if cfg.pred_wtype == "f16" and cfg.d_model % 128 == 0 and cfg.rank % 128 == 0 and n_tok > 2:
@@ -218,6 +234,9 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=20, help="replays for the per-call timing graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prompt", action="store_true", help="skip the multi-token prompt measurement")
+    ap.add_argument("--no-hot-order", action="store_true",
+                    help="keep the generated neuron order (default: place neurons by profiled hotness)")
+    ap.add_argument("--calib", type=int, default=256, help="calibration tokens per layer for the hotness profile")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -247,6 +266,8 @@ def main(argv=None):
     for li in range(L):
         lw = workload.make_layer(cfg, li, dev, args.seed)
         lw.pop("p")
+        if not args.no_hot_order:
+            lw = place_by_hotness(pi, cfg, lw, li, args.seed, args.calib, dev)
         if q4:
             # the kernels read the repacked layout; the oracle reads canonical blocks
             if li < n_base_layers and not args.no_cpu_baseline:
@@ -391,7 +412,9 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} decode batch {B}", "d_model": d, "d_ff": f, "layers": L,
                    "rank": cfg.rank, "act": cfg.act, "weights": cfg.wtype, "batch": B,
-                   "mean_density": cfg.rho, "parallelism": "none (1 GPU)"},
+                   "mean_density": cfg.rho, "parallelism": "none (1 GPU)",
+                   "neuron_order": ("as generated" if args.no_hot_order else
+                                    f"by hotness ({args.calib} calibration tokens per layer)")},
         "roofline": layer_roof,
         "roofline_parts": parts,
         "count_mean": round(cnt_mean, 1),

@@ -55,7 +55,7 @@ typedef enum pi_status {
   PI_E_SHAPE = 2,     /* a size is out of range or sizes disagree */
   PI_E_DTYPE = 3,     /* unsupported dtype, or dtype/activation combination */
   PI_E_ALIGN = 4,     /* a pointer is not 16-byte aligned */
-  PI_E_RANGE = 5,     /* tau outside (0, 1), or max_count outside [0, d_ff] */
+  PI_E_RANGE = 5,     /* tau outside (0, 1), max_count outside [0, d_ff], or overlapping buffers */
   PI_E_WORKSPACE = 6, /* ws is NULL or smaller than required */
   PI_E_HIP = 7        /* the HIP runtime refused a launch */
 } pi_status;
@@ -168,6 +168,50 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
  * cols must be a multiple of 32.  src and dst must not overlap.
  * Cited passage: [GN] "Lượng tử hóa và tương thích" (INT4 Q4_0).  */
 pi_status pi_q4_0_repack(const void* src, int32_t rows, int32_t cols, void* dst, void* stream);
+
+/* ---- Neuron placement by hotness (offline, at load time) ----------------
+ * Cited passages: [QB] "Локальность вывода, вызванная редкой активацией"
+ * (firing follows a power law: a small share of neurons carries most
+ * activations) and "Гибридный дизайн вывода CPU/GPU" (each neuron's hot or
+ * cold character is analysed in advance and decides its placement).  Here
+ * placement is a neuron's row inside its layer: pi_layer's fused kernel
+ * gives each workgroup a segment of PI_SEGMENT_ROWS consecutive neurons, and
+ * dealing hot neurons evenly over the segments evens out the active rows per
+ * workgroup.  Applying one permutation to every per-neuron array of a layer
+ * (rows of w_up, w_gate, w_down_t and p2; entries of c, b_up, b_gate) renames
+ * its neurons: the layer computes the same y up to summation order, and
+ * masks and lists then refer to the new row numbers.  */
+#define PI_SEGMENT_ROWS 32
+
+/* Firing counts of calibration tokens:
+ *   mask:   [n_tok][d_ff] u8, nonzero = active (as pi_predict writes)
+ *   counts: [d_ff] u32, device; counts[i] += number of tokens t with
+ *           mask[t][i] != 0 (accumulates over calls; the caller zeroes it).
+ * Errors: NULL pointers, n_tok < 1, d_ff < 1.  */
+pi_status pi_count_active(const uint8_t* mask, int32_t n_tok, int32_t d_ff, uint32_t* counts, void* stream);
+
+/* Placement order from firing counts.  HOST memory, synchronous, no device
+ * work: counts [d_ff], perm [d_ff] out.  perm[k] = the neuron placed at row k.
+ * Neurons sorted by count, highest first (ties: lower neuron number first),
+ * are dealt over n_seg = ceil(d_ff / PI_SEGMENT_ROWS) segments: the k-th one
+ * takes slot k / n_seg of segment k % n_seg, segments walked forward on even
+ * slots and backward on odd slots; positions past d_ff are skipped.
+ * Errors: NULL pointers, d_ff < 1.  */
+pi_status pi_hot_order(const uint32_t* counts, int32_t d_ff, int32_t* perm);
+
+/* Row permutation: dst row k = src row perm[k], k < rows.
+ *   src, dst: rows * row_bytes bytes each, device, must not overlap;
+ *             16-byte aligned
+ *   perm:     [rows] i32, device; should be a permutation of [0, rows) (an
+ *             entry outside that range gives a zero row, never a read out of
+ *             bounds)
+ *   row_bytes: a multiple of 4 (4 for a per-neuron fp32 vector).  Q4_0
+ *             weights are permuted as canonical blocks (row_bytes =
+ *             cols / 32 * 18) before pi_q4_0_repack.
+ * Errors: NULL pointers, rows < 1, row_bytes < 4 or not a multiple of 4,
+ * misaligned pointers, overlapping buffers.  */
+pi_status pi_permute_rows(const void* src, int32_t rows, int32_t row_bytes, const int32_t* perm, void* dst,
+                          void* stream);
 
 /* Static text for a status code.  */
 const char* pi_status_str(pi_status s);

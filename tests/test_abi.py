@@ -155,3 +155,19 @@ def test_repack_rejects(lib):
     assert lib.pi_q4_0_repack(FAKE, 0, 32, 0x20000, None) == L.PI_E_SHAPE
     assert lib.pi_q4_0_repack(FAKE, 4, 64, FAKE + 16, None) == L.PI_E_RANGE     # overlap
     assert lib.pi_q4_0_repack(FAKE, 1, 32, 0x20004, None) == L.PI_E_ALIGN
+
+
+def test_placement_rejects(lib):
+    assert lib.pi_count_active(None, 1, 8, FAKE, None) == L.PI_E_NULL
+    assert lib.pi_count_active(FAKE, 0, 8, 0x20000, None) == L.PI_E_SHAPE
+    assert lib.pi_count_active(FAKE, 1, 0, 0x20000, None) == L.PI_E_SHAPE
+    assert lib.pi_hot_order(None, 8, None) == L.PI_E_NULL
+    counts = (ctypes.c_uint32 * 4)()
+    perm = (ctypes.c_int32 * 4)()
+    assert lib.pi_hot_order(counts, 0, perm) == L.PI_E_SHAPE
+    assert lib.pi_permute_rows(None, 4, 16, FAKE, 0x20000, None) == L.PI_E_NULL
+    assert lib.pi_permute_rows(FAKE, 0, 16, 0x30000, 0x20000, None) == L.PI_E_SHAPE
+    assert lib.pi_permute_rows(FAKE, 4, 6, 0x30000, 0x20000, None) == L.PI_E_SHAPE
+    assert lib.pi_permute_rows(FAKE, 4, 0, 0x30000, 0x20000, None) == L.PI_E_SHAPE
+    assert lib.pi_permute_rows(FAKE_ODD, 4, 16, 0x30000, 0x20000, None) == L.PI_E_ALIGN
+    assert lib.pi_permute_rows(FAKE, 4, 16, 0x30000, FAKE + 32, None) == L.PI_E_RANGE  # overlap

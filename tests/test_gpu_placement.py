@@ -1,0 +1,113 @@
+"""GPU parity of neuron placement by hotness: firing counts and row
+permutations bit-exact against numpy, and a placed model-shaped layer against
+the oracle run on the layer as generated (placement renames neurons; the
+layer's output must not change beyond the usual tolerance).
+
+[QB] "Локальность вывода, вызванная редкой активацией" and "Гибридный дизайн
+вывода CPU/GPU": each neuron's hotness is analysed in advance and decides its
+placement.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_rank_amd as pi
+import oracle
+import workload
+from helpers import TOL, DeviceLayer, check_mask, check_y, host, oracle_sparse_chunked, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("d_ff,n_tok", [(1, 1), (3000, 5), (32768, 70)])
+def test_count_active_bitexact(d_ff, n_tok):
+    g = torch.Generator(device="cuda").manual_seed(d_ff + n_tok)
+    mask = (torch.rand((n_tok, d_ff), generator=g, device="cuda") < 0.3).to(torch.uint8)
+    mask[mask == 1] = torch.randint(1, 255, (int(mask.sum()),), generator=g, device="cuda", dtype=torch.uint8)
+    base = torch.randint(0, 1000, (d_ff,), generator=g, device="cuda", dtype=torch.int32)
+    counts = base.clone()
+    pi.count_active(mask, counts)
+    pi.count_active(mask, counts)            # accumulates
+    torch.cuda.synchronize()
+    ref = host(base).astype(np.int64) + 2 * (host(mask) != 0).sum(axis=0)
+    assert np.array_equal(host(counts).astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("shape,dtype", [((300, 8192), torch.float16), ((3000,), torch.float32),
+                                         ((257, 36), torch.uint8), ((64, 4608), torch.uint8),
+                                         ((33, 12), torch.float32)])
+def test_permute_rows_bitexact(shape, dtype):
+    rows = shape[0]
+    g = torch.Generator(device="cuda").manual_seed(rows)
+    if dtype == torch.uint8:
+        src = torch.randint(0, 256, shape, generator=g, device="cuda", dtype=torch.uint8)
+    else:
+        src = torch.randn(shape, generator=g, device="cuda").to(dtype)
+    perm = torch.randperm(rows, generator=g, device="cuda").to(torch.int32)
+    dst = pi.permute_rows(src, perm)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dst), host(src)[host(perm)])
+    # an entry outside [0, rows) gives a zero row, never a read out of bounds
+    bad = perm.clone()
+    bad[0], bad[-1] = rows, -1
+    dst2 = pi.permute_rows(src, bad)
+    torch.cuda.synchronize()
+    ref = host(src)[np.clip(host(bad), 0, rows - 1)].copy()
+    ref[0], ref[-1] = 0, 0
+    assert np.array_equal(host(dst2), ref)
+
+
+def _placed(dl: DeviceLayer, n_cal: int):
+    """Profile the layer on n_cal calibration tokens, place its neurons, and
+    return (perm, predictor, ffn) of the placed layer."""
+    cfg, L = dl.cfg, dl.L
+    xc = workload.make_tokens(cfg, 0, n_cal, "cuda", stream=9)
+    mask = torch.empty((n_cal, cfg.d_ff), dtype=torch.uint8, device="cuda")
+    pi.predict(dl.pred, xc, cfg.tau, mask)
+    counts = torch.zeros(cfg.d_ff, dtype=torch.int32, device="cuda")
+    pi.count_active(mask, counts)
+    perm = pi.hot_order(counts)
+    assert not torch.equal(perm, torch.arange(cfg.d_ff, dtype=torch.int32))
+    P = pi.place_layer(L, perm)
+    if cfg.wtype == "q4_0":
+        for k in ("w_up", "w_down_t", "w_gate"):
+            if k in P:
+                P[k] = pi.q4_0_repack(P[k], cfg.d_ff, cfg.d_model)
+    pred = pi.Predictor(P["p1"], P["p2"], P["c"])
+    ffn = pi.FFN(P["w_up"], P["w_down_t"], cfg.act, b_up=P.get("b_up"), w_gate=P.get("w_gate"),
+                 b_gate=P.get("b_gate"), d_model=cfg.d_model)
+    return host(perm).astype(np.int64), pred, ffn
+
+
+@pytest.mark.parametrize("name,n_tok", [("falcon40b", 1), ("falcon40b", 8), ("llama70b", 1), ("falcon40b_q4", 1),
+                                        ("falcon40b", 64)])
+def test_placed_layer_matches_oracle(name, n_tok):
+    cfg = workload.get_config(name)
+    dl = DeviceLayer(cfg, layer=2)
+    perm, pred, ffn = _placed(dl, n_cal=256)
+    x = workload.make_tokens(cfg, 2, n_tok, "cuda", stream=3)
+    f, d = cfg.d_ff, cfg.d_model
+    y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    pi.layer(pred, ffn, x, cfg.tau, y)
+    mask = torch.empty((n_tok, f), dtype=torch.uint8, device="cuda")
+    pi.predict(pred, x, cfg.tau, mask)
+    idx = torch.zeros(f, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pi.compact(mask, idx, cnt)
+    torch.cuda.synchronize()
+    h = dl.oracle_args()                      # the layer as generated (original neuron numbers)
+    xs = host(x)
+    ref_l, _ = oracle.predict(xs, h["p1"], h["p2"], h["c"], cfg.tau)
+    check_mask(host(mask), ref_l[:, perm], cfg.tau, f"{name} placed")
+    c = int(cnt.item())
+    orig = np.sort(perm[host(idx)[:c]])       # the listed neurons under their original numbers
+    rows = [0, n_tok - 1] if n_tok > 8 else list(range(n_tok))
+    ref_y = oracle_sparse_chunked(xs[rows], orig, h["ffn"])
+    worst = check_y(host(y)[rows], ref_y, TOL[cfg.wtype], f"{name} placed n={n_tok}")
+    print(f"{name} placed n={n_tok}: count={c} worst err={worst:.2e}", flush=True)
