@@ -84,11 +84,13 @@ def flops_ffn(cfg, cnt, n_tok):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
-def kernel_source_sha256():
-    """sha256 over include/pi.h and the kernel sources, in name order."""
+def kernel_source_sha256(names=None):
+    """sha256 over include/pi.h and the kernel sources (all of csrc/, or the
+    csrc/ files in names), in name order."""
     files = [os.path.join(ROOT, "include", "pi.h")]
     d = os.path.join(ROOT, "activation_sparse_rank_amd", "csrc")
-    files += [os.path.join(d, f) for f in sorted(os.listdir(d)) if f.endswith((".hip", ".h"))]
+    files += [os.path.join(d, f) for f in sorted(os.listdir(d))
+              if f.endswith((".hip", ".h")) and (names is None or f in names)]
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
@@ -101,8 +103,8 @@ def kernel_source_sha256():
 def load_traffic(workload):
     """HBM bytes per dispatch of each kernel, from the committed rocprofv3 PMC
     summary of this workload (profiles/*_traffic.md), or None when there is
-    none or the kernels have changed since it was taken."""
-    sha = None
+    none or the kernels have changed since it was taken (the summary names the
+    source files its kernels are built from)."""
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
         with open(path) as fh:
             m = re.search(r"```json\n(.*?)\n```", fh.read(), re.S)
@@ -111,8 +113,7 @@ def load_traffic(workload):
         data = json.loads(m.group(1))
         if data.get("workload") != workload:
             continue
-        sha = sha or kernel_source_sha256()
-        if data.get("source_sha256") != sha:
+        if data.get("source_sha256") != kernel_source_sha256(data.get("source_files")):
             return None
         fs, ws = data["fetch_scale"], data["write_scale"]
         return {k: (v["fetch_kib"] * fs + v["write_kib"] * ws) * 1024.0 for k, v in data["kernels"].items()}
