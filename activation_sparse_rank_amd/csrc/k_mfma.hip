@@ -261,6 +261,22 @@ __global__ __launch_bounds__(256) void k_xstep(const f16* __restrict__ x, int nt
       *reinterpret_cast<const u32x4*>(x + (size_t)t * d + st * kMuK + src_q * 8);
 }
 
+// As TokStep, but every lane loads: token slots past nt read the last real
+// token (a valid address; their results are never stored), so the load has
+// no lane condition and the compiler can keep it in flight.
+template <int NB>
+struct TokStepClamped {
+  u32x4 v[NB][4];
+  __device__ __forceinline__ void load(const f16* xs, int nt, int st, int g, int n16) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int t = nb * 16 + n16;
+      const int tc = t < nt ? t : nt - 1;
+      ld_k128(xs + ((size_t)st * nt + tc) * kMuK, true, g, false, v[nb]);
+    }
+  }
+};
+
 // 16-row blocks per wave in k_mup: enough rows to reuse each activation
 // operand 4 times at 64 tokens, and at few tokens few enough rows per
 // workgroup that a small union list still spreads over every CU.
@@ -334,9 +350,49 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
     }
   };
   // Two stages in flight unless their registers would crowd out the
-  // accumulators (measured: Q4_0 rows run faster with one stage).
+  // accumulators.  Q4_0 rows (18 bytes per block) are prefetched kQPre steps
+  // at a time -- every lane loads (rows past the count read a valid row whose
+  // results are never stored), so all of a chunk's loads are in flight
+  // together -- and the activation steps alternate between two register
+  // sets, the next one loading while the current one is multiplied.
   constexpr bool kPipe = !(GATED && NB > 2) && !std::is_same<WF, Q4>::value;
-  if constexpr (kPipe) {
+  if constexpr (std::is_same<WF, Q4>::value) {
+    constexpr int kQPre = 8 / MB;
+    bool all[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) all[mb] = true;
+    for (int c0 = s0; c0 < s1; c0 += kQPre) {
+      RowStep<WF, MB> up[kQPre];
+      RowStep<WF, GATED ? MB : 1> gt[GATED ? kQPre : 1];
+#pragma unroll
+      for (int j = 0; j < kQPre; ++j) {
+        const int st = c0 + j < s1 ? c0 + j : s1 - 1;
+        up[j].load(w_up, scale_off, row, all, d, st * kMuK, g);
+        if constexpr (GATED) gt[j].load(w_gate, scale_off, row, all, d, st * kMuK, g);
+      }
+      TokStepClamped<NB> xt[2];
+      xt[0].load(x, nt, c0, g, n16);
+#pragma unroll
+      for (int j = 0; j < kQPre; ++j) {
+        if (j + 1 < kQPre) xt[(j + 1) & 1].load(x, nt, c0 + j + 1 < s1 ? c0 + j + 1 : s1 - 1, g, n16);
+        if (c0 + j < s1) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            u32x4 a[4], ga[4];
+            up[j].operands(mb, a);
+            if constexpr (GATED) gt[j].operands(mb, ga);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                au[mb][nb] = mfma(a[s], xt[j & 1].v[nb][s], au[mb][nb]);
+                if constexpr (GATED) ag[mb][nb] = mfma(ga[s], xt[j & 1].v[nb][s], ag[mb][nb]);
+              }
+          }
+        }
+      }
+    }
+  } else if constexpr (kPipe) {
     Step S0, S1;
     pipeline2(s0, s1, S0, S1, load, mul);
   } else {
@@ -1162,9 +1218,13 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
 // ---------------------------------------------------------------------------
 constexpr int kMfmaTile = kMfmaTokens;
 
+// Columns per lane of k_mdown.  Q4_0 at up to 32 tokens: 16 (a column tile
+// of 256, 512 workgroups at d = 8192 with 16 chunks); measured at Q4_0
+// Falcon batch 8: 32 columns (256 workgroups) 4 us slower per layer, 8
+// columns 8 us slower.
 template <typename WF>
 constexpr int down_cpl(int nb) {
-  return std::is_same<WF, Q4>::value ? (nb == 1 ? 32 : (nb == 2 ? 16 : 8)) : 8;
+  return std::is_same<WF, Q4>::value ? (nb <= 2 ? 16 : 8) : 8;
 }
 
 // List chunks of the down projection (partial sums per chunk): the wide
