@@ -694,16 +694,27 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // The list entries of step kk+1 are loaded while step kk's rows are in
+  // flight (clamped to the last valid entry, so the loads carry no lane
+  // condition); a step then waits for one round trip, not two.
+  int nidx[8];
+  auto load_idx = [&](int kk) {
+    const int q0 = kk * 32 + g * 8;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) nidx[r] = idx[q0 + r < cnt ? q0 + r : cnt - 1];
+  };
+  if (kw0 < kw1) load_idx(kw0);
   for (int kk = kw0; kk < kw1; ++kk) {
     const int p0 = kk * 32 + g * 8;
     int rows[8];
     bool ok[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int i = p0 + r < cnt ? idx[p0 + r] : -1;
-      ok[r] = cv && (unsigned)i < (unsigned)d_ff;
+      const int i = nidx[r];
+      ok[r] = cv && p0 + r < cnt && (unsigned)i < (unsigned)d_ff;
       rows[r] = ok[r] ? i : 0;
     }
+    if (kk + 1 < kw1) load_idx(kk + 1);
     DownRows<WF, CPL> wr;
     wr.load(w_dt, scale_off, d, rows, ok, col);
     u32x4 a[NB];
