@@ -203,7 +203,8 @@ def _pred_kernels(cfg, n_tok):
 def _ffn_kernels(cfg, n_tok):
     """Kernels of one pi_sparse_ffn call (labels only)."""
     q4 = cfg.wtype == "q4_0"
-    if n_tok > _tile(cfg) and cfg.wtype in ("f16", "q4_0") and cfg.d_model % 128 == 0:
+    mfma_from = 3 if cfg.wtype == "f16" else _tile(cfg) + 1
+    if n_tok >= mfma_from and cfg.wtype in ("f16", "q4_0") and cfg.d_model % 128 == 0:
         wide = min(n_tok, 64) > 32
         return f"k_xstep + {'k_mup_wide + k_mfin + k_mdown_wide' if wide else 'k_mup + k_mdown'} + k_merge"
     return f"k_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
