@@ -1235,12 +1235,18 @@ constexpr int kMfmaTile = kMfmaTokens;
 // columns 8 us slower.
 template <typename WF>
 constexpr int down_cpl(int nb) {
-  return std::is_same<WF, Q4>::value ? (nb <= 2 ? 16 : 8) : 8;
+  return std::is_same<WF, Q4>::value ? (nb <= 1 ? 16 : 8) : 8;
 }
 
 // List chunks of the down projection (partial sums per chunk): the wide
 // kernel (33-64 tokens) needs 32 for 2 workgroups per CU.
-int mfma_chunks(int wtype, int nb) { return nb >= 3 ? 32 : (wtype == 2 ? 16 : 8); }
+// Token blocks (of 16) from which the wide kernels (k_mup_wide + k_mfin,
+// k_mdown_wide) take over: 3 for fp16 rows, 2 for Q4_0 rows.
+template <typename WF>
+constexpr int wide_from() { return std::is_same<WF, Q4>::value ? 2 : 3; }
+int wide_nb(int wtype) { return wtype == 2 ? 2 : 3; }
+
+int mfma_chunks(int wtype, int nb) { return nb >= wide_nb(wtype) ? 32 : (wtype == 2 ? 16 : 8); }
 
 // k splits of the predictor's first product: about 4 steps of 128 per split.
 int pred_splits(int d) {
@@ -1273,7 +1279,7 @@ WideWs wide_ws(const SparseArgs& a) {
 
 template <typename WF, int ACT, int NB>
 hipError_t launch_mup(const SparseArgs& a, const f16* x, int nt, f16* h, int ldh, hipStream_t s) {
-  if constexpr (NB >= 3) {
+  if constexpr (NB >= wide_from<WF>()) {
     const int grid = (a.max_count + kMxRows - 1) / kMxRows;
     if (grid == 0) return hipSuccess;
     const size_t so = std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
@@ -1326,7 +1332,7 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
   constexpr int CPL = down_cpl<WF>(NB);
   const int chunks = mfma_chunks(a.wtype, NB);
   const size_t so = std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
-  if constexpr (NB >= 3) {
+  if constexpr (NB >= wide_from<WF>()) {
     const int tile = kMdWaves * 16 * CPL;
     const dim3 grid((a.d + tile - 1) / tile, chunks);
     hipLaunchKernelGGL((k_mdown_wide<WF, NB, CPL>), grid, dim3(kMdThreads), 0, s, a.w_down_t, so, a.d, a.d_ff, a.idx,
@@ -1428,7 +1434,7 @@ void mfma_workspace(int wtype, int d, int d_ff, int n_tok, size_t* h_bytes, size
   const int nt = n_tok < kMfmaTile ? n_tok : kMfmaTile;
   const int nb = (nt + 15) / 16;
   (void)nb;
-  *h_bytes = h_region(d_ff, 4) + xs_region(d) + (nb >= 3 ? wide_region(d_ff) : 0);
+  *h_bytes = h_region(d_ff, 4) + xs_region(d) + (nb >= wide_nb(wtype) ? wide_region(d_ff) : 0);
   *part_bytes = (size_t)mfma_chunks(wtype, nb) * nt * d * sizeof(float);
 }
 
