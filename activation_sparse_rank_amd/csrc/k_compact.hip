@@ -20,6 +20,7 @@ namespace {
 constexpr int kCThreads = 1024;
 constexpr int kCWaves = kCThreads / kWave;
 constexpr int kCBytes = 16;    // mask bytes per thread per tile
+constexpr int kCTok = 8;       // token rows in flight per thread
 
 // Bit b (b < 4) of the result is set when byte b of v is nonzero.
 __device__ __forceinline__ unsigned nz_bytes4(unsigned v) {
@@ -45,8 +46,21 @@ __global__ __launch_bounds__(kCThreads) void k_compact(const uint8_t* __restrict
     unsigned flags = 0;
     if (p < d_ff) {
       if (vec_ok && p + kCBytes <= d_ff) {
+        // kCTok token rows per round, all loads in flight together; past the
+        // last token the last row is read again (OR is idempotent), so the
+        // loads carry no condition.
         u32x4 acc = {0, 0, 0, 0};
-        for (int t = 0; t < n_tok; ++t) acc |= ld16(mask + (size_t)t * d_ff + p);
+        if (n_tok == 1) acc = ld16(mask + p);
+        else for (int t0 = 0; t0 < n_tok; t0 += kCTok) {
+          u32x4 v[kCTok];
+#pragma unroll
+          for (int u = 0; u < kCTok; ++u) {
+            const int t = t0 + u < n_tok ? t0 + u : n_tok - 1;
+            v[u] = ld16(mask + (size_t)t * d_ff + p);
+          }
+#pragma unroll
+          for (int u = 0; u < kCTok; ++u) acc |= v[u];
+        }
         flags = nz_bytes4(acc.x) | (nz_bytes4(acc.y) << 4) | (nz_bytes4(acc.z) << 8) | (nz_bytes4(acc.w) << 12);
       } else {
         const int nb = d_ff - p < kCBytes ? d_ff - p : kCBytes;
