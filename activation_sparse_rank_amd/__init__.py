@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     layer,
     permute_rows,
     place_layer,
+    stream_read,
     predict,
     q4_0_repack,
     sparse_ffn,

@@ -22,10 +22,11 @@ STATUS_NAMES = {
 
 # Every symbol include/pi.h declares.
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_layer",
-           "pi_q4_0_repack", "pi_count_active", "pi_hot_order", "pi_permute_rows", "pi_status_str",
+           "pi_q4_0_repack", "pi_count_active", "pi_hot_order", "pi_permute_rows", "pi_stream_read", "pi_status_str",
            "pi_last_error")
 
 PI_SEGMENT_ROWS = 32   # neurons per segment of pi_layer's fused kernel (pi.h)
+PI_STREAM_BLOCKS = 2048  # entries of pi_stream_read's output (pi.h)
 
 
 class PiPredictor(ctypes.Structure):
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pi_hot_order.restype = ctypes.c_int
     lib.pi_permute_rows.argtypes = [P, i32, i32, P, P, P]
     lib.pi_permute_rows.restype = ctypes.c_int
+    lib.pi_stream_read.argtypes = [P, sz, P, P]
+    lib.pi_stream_read.restype = ctypes.c_int
     lib.pi_status_str.argtypes = [ctypes.c_int]
     lib.pi_status_str.restype = ctypes.c_char_p
     lib.pi_last_error.argtypes = []

@@ -288,3 +288,18 @@ def place_layer(tensors: dict, perm) -> dict:
             pd = perm.to(device=t.device, dtype=torch.int32).contiguous()
         out[k] = permute_rows(t, pd)
     return out
+
+
+def stream_read(src, out=None, stream=None):
+    """Read every byte of src once (pi_stream_read); returns out, whose XOR
+    over its PI_STREAM_BLOCKS int32 entries is the XOR of src's 32-bit words."""
+    _dev(src, "src")
+    nbytes = src.numel() * src.element_size()
+    if out is None:
+        out = torch.empty(L.PI_STREAM_BLOCKS, dtype=torch.int32, device=src.device)
+    _dev(out, "out")
+    if out.dtype != torch.int32 or out.numel() != L.PI_STREAM_BLOCKS:
+        raise ValueError("out must be int32 [PI_STREAM_BLOCKS]")
+    st = L.load().pi_stream_read(src.data_ptr(), nbytes, out.data_ptr(), _stream(stream))
+    _check(st, "pi_stream_read")
+    return out

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpi.so")
 
-SOURCES = ["abi.hip", "k_predict.hip", "k_compact.hip", "k_gather.hip", "k_mfma.hip", "k_q4.hip", "k_place.hip"]
+SOURCES = ["abi.hip", "k_predict.hip", "k_compact.hip", "k_gather.hip", "k_mfma.hip", "k_q4.hip", "k_place.hip", "k_stream.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -324,6 +324,15 @@ pi_status pi_permute_rows(const void* src, int32_t rows, int32_t row_bytes, cons
   return PI_OK;
 }
 
+pi_status pi_stream_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  if (!src || !out) return PI_E_NULL;
+  if (bytes == 0 || bytes % 16) return PI_E_SHAPE;
+  if (!al16(src)) return PI_E_ALIGN;
+  const hipError_t e = pi::launch_stream_read(src, bytes, out, PI_STREAM_BLOCKS, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
 const char* pi_status_str(pi_status s) {
   switch (s) {
     case PI_OK: return "ok";

@@ -187,4 +187,8 @@ void hot_order(const uint32_t* counts, int d_ff, int seg, int32_t* perm);
 hipError_t launch_permute_rows(const void* src, int rows, int row_bytes, const int32_t* perm, void* dst,
                                hipStream_t s);
 
+// Streaming read of bytes of src by blocks workgroups; out[b] = XOR of the
+// 32-bit words workgroup b read (k_stream.hip).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* out, int blocks, hipStream_t s);
+
 }  // namespace pi

@@ -177,6 +177,24 @@ def _tile(cfg):
     return t
 
 
+def measure_stream(pi, dev, stream, nbytes=8 << 30, reps=10):
+    """GB/s of pi_stream_read over an nbytes buffer (event-timed on stream)."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(pi._lib.PI_STREAM_BLOCKS, dtype=torch.int32, device=dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        pi.stream_read(buf, out)
+        start.record(stream)
+        for _ in range(reps):
+            pi.stream_read(buf, out)
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del buf
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def place_by_hotness(pi, cfg, lw, layer, seed, n_cal, dev):
     """Offline placement of one layer's neurons: run the layer's predictor on
     n_cal calibration tokens (a token stream of their own, never timed),
@@ -385,6 +403,10 @@ def main(argv=None):
                 "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_of(kernels),
                 "bytes_per_launch": int(b), "avg_launch_us": round(ms * 1e3, 3)}
 
+    # achievable HBM read bandwidth: a plain streaming read (pi_stream_read)
+    # of an 8 GiB buffer, the reference the path's streams are compared with
+    stream_gbps = measure_stream(pi, dev, stream)
+
     # whole-layer bytes per layer call, averaged over the timed steps
     b_layer = float(np.mean([bytes_layer(cfg, c, B) for c in counts.flat]))
     ms_layer = ms_step / L
@@ -396,6 +418,9 @@ def main(argv=None):
                     "bytes_per_launch": int(b_comp)},
         "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, B)})", b_sp, ms_sp),
     }
+    for r in (layer_roof, parts["predict"], parts["gather"]):
+        r["stream_read_gbps"] = stream_gbps
+        r["frac_of_stream_read"] = round(r["achieved"] / stream_gbps, 4)
     parts["gather"]["active_weight_gbps"] = round(b_act / (ms_sp * 1e-3) / 1e9, 1)
     parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
 

@@ -213,6 +213,19 @@ pi_status pi_hot_order(const uint32_t* counts, int32_t d_ff, int32_t* perm);
 pi_status pi_permute_rows(const void* src, int32_t rows, int32_t row_bytes, const int32_t* perm, void* dst,
                           void* stream);
 
+/* ---- Measurement aid ----------------------------------------------------
+ * Not an operation of the method: a plain streaming read of a device buffer,
+ * the achievable HBM read bandwidth against which the path's own streams and
+ * gathers are reported.
+ *   src:   bytes of device memory, 16-byte aligned; bytes a positive
+ *          multiple of 16
+ *   out:   [PI_STREAM_BLOCKS] u32, device; out[b] = XOR of the 32-bit words
+ *          that workgroup b read, so the XOR over out[] is the XOR of every
+ *          32-bit word of src (a check that every byte was read).
+ * Errors: NULL pointers, bytes 0 or not a multiple of 16, misaligned src.  */
+#define PI_STREAM_BLOCKS 2048
+pi_status pi_stream_read(const void* src, size_t bytes, uint32_t* out, void* stream);
+
 /* Static text for a status code.  */
 const char* pi_status_str(pi_status s);
 

@@ -171,3 +171,10 @@ def test_placement_rejects(lib):
     assert lib.pi_permute_rows(FAKE, 4, 0, 0x30000, 0x20000, None) == L.PI_E_SHAPE
     assert lib.pi_permute_rows(FAKE_ODD, 4, 16, 0x30000, 0x20000, None) == L.PI_E_ALIGN
     assert lib.pi_permute_rows(FAKE, 4, 16, 0x30000, FAKE + 32, None) == L.PI_E_RANGE  # overlap
+
+
+def test_stream_read_rejects(lib):
+    assert lib.pi_stream_read(None, 16, FAKE, None) == L.PI_E_NULL
+    assert lib.pi_stream_read(FAKE, 0, 0x20000, None) == L.PI_E_SHAPE
+    assert lib.pi_stream_read(FAKE, 24, 0x20000, None) == L.PI_E_SHAPE
+    assert lib.pi_stream_read(FAKE_ODD, 32, 0x20000, None) == L.PI_E_ALIGN

@@ -111,3 +111,16 @@ def test_placed_layer_matches_oracle(name, n_tok):
     ref_y = oracle_sparse_chunked(xs[rows], orig, h["ffn"])
     worst = check_y(host(y)[rows], ref_y, TOL[cfg.wtype], f"{name} placed n={n_tok}")
     print(f"{name} placed n={n_tok}: count={c} worst err={worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 1 << 20, (64 << 20) + 16])
+def test_stream_read_reads_every_word(nbytes):
+    # The bandwidth reference reads each byte once: the XOR of its per-block
+    # results equals the XOR of every 32-bit word of the buffer.
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, device="cuda", dtype=torch.int32)
+    out = pi.stream_read(buf)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(host(out).view(np.uint32))
+    ref = np.bitwise_xor.reduce(host(buf).view(np.uint32))
+    assert got == ref
