@@ -1,0 +1,38 @@
+"""The benchmark's algorithmic byte counts (the roofline numerators), written
+out by hand for the model shapes: per layer call at batch 1, the predictor
+(p1 [r][d] and p2 [d_ff][r] in fp16, c fp32), the active rows of the FFN
+matrices (one row per listed neuron per matrix: 2 bytes per weight for fp16,
+18 bytes per 32 weights for Q4_0), a bias and a list entry per listed neuron,
+x in and y (fp32) out.  CPU only."""
+
+import bench
+import workload
+
+
+def _by_hand(d, d_ff, r, n_mat, row_bytes, cnt, x_bytes=2):
+    pred = (r * d + d_ff * r) * 2 + 4 * d_ff
+    active = cnt * n_mat * row_bytes
+    return pred + active + 8 * cnt + d * x_bytes + 4 * d
+
+
+def test_falcon_fp16_layer_bytes():
+    cfg = workload.get_config("falcon40b")
+    cnt = 3277
+    assert bench.bytes_layer(cfg, cnt) == _by_hand(8192, 32768, 1024, 2, 8192 * 2, cnt)
+    # about 191.5 MB at the mean list length: 84.0 MB of predictor, 107.4 MB of rows
+    assert abs(bench.bytes_layer(cfg, cnt) / 1e6 - 191.5) < 0.2
+    assert bench.bytes_active(cfg, cnt) == 3277 * 2 * 16384
+
+
+def test_llama_reglu_and_q4_layer_bytes():
+    cfg = workload.get_config("llama70b")
+    assert bench.bytes_layer(cfg, 2867) == _by_hand(8192, 28672, 1024, 3, 8192 * 2, 2867)
+    q = workload.get_config("falcon40b_q4")
+    assert bench.bytes_active(q, 3277) == 3277 * 2 * (8192 // 32 * 18)
+    assert bench.bytes_layer(q, 3277) == _by_hand(8192, 32768, 1024, 2, 4608, 3277)
+
+
+def test_gather_and_predict_bytes():
+    cfg = workload.get_config("falcon40b")
+    assert bench.bytes_gather(cfg, 100) == 100 * 2 * 16384 + 800 + 8192 * 2 + 8192 * 4
+    assert bench.bytes_predict(cfg) == (1024 * 8192 + 32768 * 1024) * 2 + 4 * 32768 + 8192 * 2 + 32768
