@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     PiError,
     Predictor,
     alloc_workspace,
+    clear_flags,
     compact,
     count_active,
     hot_order,
@@ -19,6 +20,7 @@ from .api import (  # noqa: F401
     stream_read,
     predict,
     q4_0_repack,
+    read_flags,
     sparse_ffn,
     workspace_bytes,
 )

@@ -134,7 +134,35 @@ def workspace_bytes(pred: Predictor | None, ffn: FFN | None, n_tok: int) -> int:
 
 
 def alloc_workspace(pred, ffn, n_tok, device="cuda") -> torch.Tensor:
-    return torch.empty(workspace_bytes(pred, ffn, n_tok), dtype=torch.uint8, device=device)
+    """A zero-filled workspace (so its fault flags start clear)."""
+    return torch.zeros(workspace_bytes(pred, ffn, n_tok), dtype=torch.uint8, device=device)
+
+
+def _temp_workspace(pred, ffn, n_tok, device, stream):
+    """Workspace for one call that was given none.  It is allocated on the
+    call's stream, so that when the tensor is freed right after the call the
+    caching allocator hands its memory out again only in that stream's
+    order, after the call's kernels."""
+    if stream is None:
+        return alloc_workspace(pred, ffn, n_tok, device)
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+    with torch.cuda.stream(s):
+        return alloc_workspace(pred, ffn, n_tok, device)
+
+
+def clear_flags(ws, stream=None):
+    """Zero the workspace header: fault flags and test hooks (pi_clear_flags)."""
+    _dev(ws, "ws")
+    _check(L.load().pi_clear_flags(ws.data_ptr(), _stream(stream)), "pi_clear_flags")
+
+
+def read_flags(ws, stream=None) -> int:
+    """The workspace's sticky fault flags (PI_FLAG_* bits) after the work
+    queued on stream (pi_read_flags; synchronises that stream)."""
+    _dev(ws, "ws")
+    out = ctypes.c_uint32(0)
+    _check(L.load().pi_read_flags(ws.data_ptr(), ctypes.byref(out), _stream(stream)), "pi_read_flags")
+    return int(out.value)
 
 
 def _x(x, d, dtype, name="x"):
@@ -156,7 +184,7 @@ def predict(pred: Predictor, x, tau: float, mask, logits=None, ws=None, stream=N
         if logits.dtype != torch.float32 or logits.shape != (n, pred.d_ff):
             raise ValueError("logits must be float32 [n_tok, d_ff]")
     if ws is None:
-        ws = alloc_workspace(pred, None, n, x.device)
+        ws = _temp_workspace(pred, None, n, x.device, stream)
     _dev(ws, "ws")
     st = L.load().pi_predict(ctypes.byref(pred.desc), x.data_ptr(), _DTYPES[x.dtype], n, float(tau),
                              mask.data_ptr(), _ptr(logits), ws.data_ptr(), ws.numel(), _stream(stream))
@@ -187,7 +215,7 @@ def sparse_ffn(ffn: FFN, x, idx, count, y, ws=None, max_count=None, stream=None)
     if idx.numel() < min(mc, ffn.d_ff):
         raise ValueError("idx is shorter than max_count")
     if ws is None:
-        ws = alloc_workspace(None, ffn, n, x.device)
+        ws = _temp_workspace(None, ffn, n, x.device, stream)
     _dev(ws, "ws")
     st = L.load().pi_sparse_ffn(ctypes.byref(ffn.desc), x.data_ptr(), _DTYPES[x.dtype], n, idx.data_ptr(),
                                 count.data_ptr(), mc, y.data_ptr(), _DTYPES[y.dtype], ws.data_ptr(),
@@ -201,7 +229,7 @@ def layer(pred: Predictor, ffn: FFN, x, tau: float, y, ws=None, stream=None):
     if y.dtype not in _DTYPES or y.shape != (n, ffn.d_model):
         raise ValueError("y must be float32 or float16 [n_tok, d_model]")
     if ws is None:
-        ws = alloc_workspace(pred, ffn, n, x.device)
+        ws = _temp_workspace(pred, ffn, n, x.device, stream)
     _dev(ws, "ws")
     st = L.load().pi_layer(ctypes.byref(pred.desc), ctypes.byref(ffn.desc), x.data_ptr(), _DTYPES[x.dtype], n,
                            float(tau), y.data_ptr(), _DTYPES[y.dtype], ws.data_ptr(), ws.numel(),

@@ -52,8 +52,10 @@ pi_status check_ffn(const pi_ffn* f) {
 
 int x_type_of(const pi_ffn* f) { return f->wtype == PI_Q4_0 ? PI_F16 : f->wtype; }
 
-// Workspace: each entry point lays out only the sections it uses, in this
-// order, every section 256-byte aligned.
+// Workspace: the header (pi.h), then only the sections the entry point uses,
+// in this order, every section 256-byte aligned.  The status section holds
+// one counter per segment of the in-kernel list and, after them, the
+// per-call fault word.
 struct Layout {
   size_t t = 0, tpart = 0, mask = 0, idx = 0, count = 0, status = 0, h = 0, part = 0;
   size_t total = 0;
@@ -68,6 +70,7 @@ Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
     off += up256(bytes);
     return o;
   };
+  take(PI_WS_HEADER_BYTES);
   if (pred) {
     L.t = take((size_t)n_tok * pred->rank * sizeof(float));
     if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok))
@@ -78,7 +81,7 @@ Layout layout(const pi_predictor* pred, const pi_ffn* ffn, int n_tok) {
     L.idx = take((size_t)ffn->d_ff * sizeof(int32_t));
     L.count = take(sizeof(int32_t));
     L.n_segments = pi::layer_segments(ffn->d_ff);
-    L.status = take((size_t)L.n_segments * sizeof(unsigned));
+    L.status = take(((size_t)L.n_segments + 1) * sizeof(unsigned));
   }
   if (ffn) {
     const int tile = pi::sparse_tile(ffn->wtype, ffn->d_model);
@@ -125,7 +128,7 @@ hipError_t predict_any(const pi_predictor* pred, const void* x, int n_tok, float
   if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok))
     return pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
                                    theta, t, ws + L.tpart, mask, logits, nullptr, nullptr, 0, nullptr, nullptr,
-                                   nullptr, s);
+                                   reinterpret_cast<unsigned*>(ws), nullptr, nullptr, s);
   hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, nullptr,
                                            0, s);
   if (e != hipSuccess) return e;
@@ -156,6 +159,8 @@ pi::SparseArgs sparse_args(const pi_ffn* f, const void* x, int n_tok, const int3
   a.part = reinterpret_cast<float*>(ws + L.part);
   a.n_chunks = L.n_chunks;
   a.n_slices = L.n_slices;
+  a.flags = reinterpret_cast<unsigned*>(ws);     // the header's flags word
+  a.fault = nullptr;
   return a;
 }
 
@@ -240,15 +245,21 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
   int32_t* idx = reinterpret_cast<int32_t*>(w + L.idx);
   int32_t* count = reinterpret_cast<int32_t*>(w + L.count);
   unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
+  unsigned* fault = status + L.n_segments;
+  unsigned* hdr = reinterpret_cast<unsigned*>(w);
   const hipStream_t s = as_stream(stream);
   pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
+  // The fused kernel takes one token tile of the list path; where either
+  // stand-alone call would take the matrix cores, the layer does too, so that
+  // pi_layer always equals pi_predict + pi_compact + pi_sparse_ffn bit for bit.
   const bool fused = n_tok <= pi::sparse_tile(ffn->wtype, ffn->d_model) && n_tok <= pi::pred_tile(pred->rank) &&
-                     !pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok);
+                     !pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok) &&
+                     !pi::mfma_path(ffn->wtype, ffn->d_model, n_tok);
   hipError_t e;
   if (fused) {
-    // Stage 1 also clears the fused kernel's segment counters.
+    // Stage 1 also clears the fused kernel's segment counters and the fault word after them.
     e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, status,
-                                  L.n_segments, s);
+                                  L.n_segments + 1, s);
     if (e != hipSuccess) return hip_fail(e);
     pi::LayerArgs la;
     la.p2 = pred->p2;
@@ -259,6 +270,9 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
     la.status = status;
     la.idx = idx;
     la.count = count;
+    la.hdr = hdr;
+    la.fault = fault;
+    a.fault = fault;
     e = pi::launch_layer_fused(a, la, s);
     if (e != hipSuccess) return hip_fail(e);
     return PI_OK;
@@ -271,8 +285,9 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
     const void* xs = nullptr;
     e = pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
                                 theta_of(tau), t, w + L.tpart, nullptr, nullptr, mask, status, L.n_segments, idx,
-                                count, &xs, s);
+                                count, hdr, fault, &xs, s);
     a.xs_pre = xs;
+    a.fault = fault;
   } else {
     e = predict_any(pred, x, n_tok, theta_of(tau), t, w, L, mask, nullptr, s);
     if (e != hipSuccess) return hip_fail(e);
@@ -329,6 +344,25 @@ pi_status pi_stream_read(const void* src, size_t bytes, uint32_t* out, void* str
   if (bytes == 0 || bytes % 16) return PI_E_SHAPE;
   if (!al16(src)) return PI_E_ALIGN;
   const hipError_t e = pi::launch_stream_read(src, bytes, out, PI_STREAM_BLOCKS, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_clear_flags(void* ws, void* stream) {
+  if (!ws) return PI_E_NULL;
+  if (!al16(ws)) return PI_E_ALIGN;
+  const hipError_t e = pi::launch_clear_header(static_cast<unsigned*>(ws), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_read_flags(const void* ws, uint32_t* flags, void* stream) {
+  if (!ws || !flags) return PI_E_NULL;
+  if (!al16(ws)) return PI_E_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = hipMemcpyAsync(flags, static_cast<const unsigned*>(ws) + PI_WS_FLAGS, sizeof(uint32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
   return PI_OK;
 }

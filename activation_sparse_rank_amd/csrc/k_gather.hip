@@ -272,9 +272,10 @@ __global__ __launch_bounds__(kUpThreads) void k_up(const void* __restrict__ w_up
 // dispatched before it, so the grid needs no co-residency.  The list equals
 // pi_compact's (ascending neuron numbers) and h is stored by list position,
 // so the down projection sees the same inputs on both paths.
-// status[] must be zero at launch (the first predictor stage clears it).
-// Every wait is bounded: after kSpinLimit polls the kernel moves on, so the
-// grid always drains.
+// status[] and *fault must be zero at launch (the first predictor stage
+// clears them).  Every wait is bounded (hdr[PI_WS_WAIT_POLLS] polls, or
+// kDefaultWaitPolls), so the grid always drains; a wait that runs out sets
+// *fault (the merge then writes NaN) and PI_FLAG_WAIT_EXPIRED in hdr[0].
 // ---------------------------------------------------------------------------
 constexpr int kPUThreads = 256;
 constexpr int kPUWaves = kPUThreads / kWave;
@@ -283,7 +284,7 @@ constexpr int kPURows = kPUThreads / kP2Group * kPUSub;               // 32 neur
 static_assert(kPURows == PI_SEGMENT_ROWS, "the segment size pi_hot_order deals neurons over");
 constexpr int kPULoads = 8;                                           // status loads per thread per batch
 constexpr unsigned kReady = 0x80000000u;
-constexpr int kSpinLimit = 1 << 16;
+constexpr int kExpiredBit = 0x40000000;                                // > any count (d_ff < 2^30)
 // Rows per phase-C batch (ReLU; ReGLU half as many).  A fp16 row part is 64
 // bytes per lane, a Q4_0 row part 18: Q4_0 batches hold 3x as many rows in
 // the same registers, so a segment with many active neurons needs fewer
@@ -299,14 +300,15 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
                                                         const float* __restrict__ bias, const W* __restrict__ x,
                                                         int d, int nt, unsigned* __restrict__ status,
                                                         int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                                                        float* __restrict__ h) {
+                                                        float* __restrict__ h, unsigned* __restrict__ hdr,
+                                                        unsigned* __restrict__ fault) {
   extern __shared__ float smem[];    // t tile [NT][rank], then (XL) x tile [NT][d/E] chunks
   float* t_lds = smem;
   u32x4* x_lds = reinterpret_cast<u32x4*>(smem + NT * rank);
   __shared__ int act_lds[kPURows];
   __shared__ float pu_lds[kPUWaves][kPURows][NT];                     // part sums of phase C
   __shared__ float pg_lds[ACT == ACT_REGLU ? kPUWaves : 1][kPURows][NT];
-  __shared__ int red_lds[kPUWaves];
+  __shared__ int red_lds[kPUWaves];       // phase D: per-wave count sums, kExpiredBit if a wait ran out
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane & (kP2Group - 1);
@@ -314,6 +316,8 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   const int wg = blockIdx.x;
   const int seg0 = wg * kPURows;
   const char* xb = reinterpret_cast<const char*>(x);
+  const unsigned polls_hook = hdr[PI_WS_WAIT_POLLS], skip_hook = hdr[PI_WS_SKIP_PUBLISH];
+  const int max_polls = polls_hook ? (int)polls_hook : kDefaultWaitPolls;
 
   // ---- A: logits ----
   int rows[kPUSub];
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   const int n_g = __builtin_popcountll(am);
 
   // ---- B: publish this workgroup's count ----
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0 && skip_hook != (unsigned)wg + 1u)
     __hip_atomic_store(&status[wg], kReady | (unsigned)n_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- C: up projection of the active neurons: wave q computes part q of
@@ -386,6 +390,7 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   // Each thread reads its share of status[0 .. wg-1] kPULoads at a time, all
   // loads of a batch in flight together.
   int part = 0;
+  bool expired = false;
   for (int p0 = 0; p0 < wg; p0 += kPUThreads * kPULoads) {
     unsigned v[kPULoads];
 #pragma unroll
@@ -396,20 +401,29 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
 #pragma unroll
     for (int u = 0; u < kPULoads; ++u) {
       const int p = p0 + u * kPUThreads + (int)threadIdx.x;
-      for (int spin = 0; !(v[u] & kReady) && spin < kSpinLimit; ++spin) {
+      for (int spin = 0; !(v[u] & kReady) && spin < max_polls; ++spin) {
         __builtin_amdgcn_s_sleep(2);
         v[u] = __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      expired |= !(v[u] & kReady);
       part += (int)(v[u] & ~kReady);
     }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
-  if (lane == 0) red_lds[wave] = part;
+  const bool wave_expired = __ballot(expired) != 0ull;
+  if (lane == 0) red_lds[wave] = part | (wave_expired ? kExpiredBit : 0);
   __syncthreads();   // also orders the part sums of phase C before their reads below
-  int off = 0;
+  int off = 0, any_expired = 0;
 #pragma unroll
-  for (int w = 0; w < kPUWaves; ++w) off += red_lds[w];
+  for (int w = 0; w < kPUWaves; ++w) {
+    off += red_lds[w] & ~kExpiredBit;
+    any_expired |= red_lds[w] & kExpiredBit;
+  }
+  if (any_expired && threadIdx.x == 0) {
+    raise_flag(fault, 1u);
+    raise_flag(hdr + PI_WS_FLAGS, PI_FLAG_WAIT_EXPIRED);
+  }
   if (wave == 0) {
     const bool mine = lane < kPURows && ((am >> lane) & 1ull);
     const int pos = off + __builtin_popcountll(am & ((1ull << lane) - 1ull));
@@ -680,7 +694,8 @@ __host__ __device__ constexpr int merge_group(int n_chunks) {
 }
 
 __global__ __launch_bounds__(kMgThreads) void k_merge(const float* __restrict__ part, int n_chunks, int n,
-                                                      void* __restrict__ y, int ytype) {
+                                                      void* __restrict__ y, int ytype,
+                                                      const unsigned* __restrict__ fault) {
   __shared__ float buf[kMgThreads * 4];
   const int G = merge_group(n_chunks);
   const int QW = kMgThreads / G;                 // 16-byte quads per workgroup
@@ -693,15 +708,20 @@ __global__ __launch_bounds__(kMgThreads) void k_merge(const float* __restrict__ 
   reinterpret_cast<float4*>(buf)[threadIdx.x] = v;   // buf[g][4q .. 4q+3]
   __syncthreads();
   const int o = threadIdx.x;
+  const bool poison = fault != nullptr && *fault != 0u;
   if (o < ncol && col0 + o < n) {
     float s = 0.f;
     for (int c = 0; c < n_chunks; ++c) s += buf[c * ncol + o];
+    if (poison) s = __builtin_nanf("");
     if (ytype == 1)
       static_cast<f16*>(y)[col0 + o] = (f16)s;
     else
       static_cast<float*>(y)[col0 + o] = s;
   }
 }
+
+// Zero a workspace header (one thread per word).
+__global__ __launch_bounds__(kHdrWords) void k_clear_header(unsigned* __restrict__ hdr) { hdr[threadIdx.x] = 0u; }
 
 // ---------------------------------------------------------------------------
 // Host side
@@ -727,7 +747,7 @@ hipError_t launch_down(const SparseArgs& a, void* y, int nt, hipStream_t s) {
                        a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_merge(a.part, a.n_chunks, nt * a.d, y, a.ytype, s);
+  return launch_merge(a.part, a.n_chunks, nt * a.d, y, a.ytype, a.fault, s);
 }
 
 // x is staged in LDS when its token tile fits in 32 KB.
@@ -766,11 +786,12 @@ hipError_t launch_pred_up(const SparseArgs& a, const LayerArgs& L, const typenam
   if (x_in_lds<X>(NT, a.d)) {
     const size_t lds = lds_t + (size_t)NT * a.d * sizeof(X);
     hipLaunchKernelGGL((k_pred_up<X, WF, ACT, NT, true>), dim3(grid), dim3(kPUThreads), lds, s, p2, L.c, L.t, L.rank,
-                       a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.status, L.idx, L.count, a.h);
+                       a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.status, L.idx, L.count, a.h,
+                       L.hdr, L.fault);
   } else {
     hipLaunchKernelGGL((k_pred_up<X, WF, ACT, NT, false>), dim3(grid), dim3(kPUThreads), lds_t, s, p2, L.c, L.t,
                        L.rank, a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.status, L.idx, L.count,
-                       a.h);
+                       a.h, L.hdr, L.fault);
   }
   return hipGetLastError();
 }
@@ -854,13 +875,20 @@ void sparse_chunking(int wtype, int d, int* n_chunks, int* n_slices) {
 
 int layer_segments(int d_ff) { return (d_ff + kPURows - 1) / kPURows; }
 
-hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, hipStream_t s) {
+hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, const unsigned* fault,
+                        hipStream_t s) {
   if (n <= 0) return hipSuccess;
   // The merge reads whole 16-byte quads of the partials.
   if (n_chunks < 1 || n_chunks > kMgMaxChunks || n % 4 != 0 || (reinterpret_cast<uintptr_t>(part) & 15) != 0)
     return hipErrorInvalidValue;
   const int ncol = 4 * (kMgThreads / merge_group(n_chunks));
-  hipLaunchKernelGGL(k_merge, dim3((n + ncol - 1) / ncol), dim3(kMgThreads), 0, s, part, n_chunks, n, y, ytype);
+  hipLaunchKernelGGL(k_merge, dim3((n + ncol - 1) / ncol), dim3(kMgThreads), 0, s, part, n_chunks, n, y, ytype,
+                     fault);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_header(unsigned* hdr, hipStream_t s) {
+  hipLaunchKernelGGL(k_clear_header, dim3(1), dim3(kHdrWords), 0, s, hdr);
   return hipGetLastError();
 }
 

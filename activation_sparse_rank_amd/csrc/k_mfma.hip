@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
                                                     const f16* __restrict__ x, int d, int d_ff, int nt,
                                                     const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ count_ptr, int max_count,
-                                                    f16* __restrict__ h, int ldh) {
+                                                    f16* __restrict__ h, int ldh, unsigned* __restrict__ flags) {
   constexpr bool GATED = ACT == ACT_REGLU;
   constexpr int MB = mup_mb<NB>();
   constexpr int NQ = MB * NB;              // accumulator quads per lane
@@ -421,6 +421,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
     sum_waves<NQ>(&red[0][0][0][0], flat, su);
   }
 
+  bool over = false;                       // an H value not finite in fp16
 #pragma unroll
   for (int e = 0; e < QT; ++e) {
     const int q = oq + kMuWaves * e;
@@ -439,6 +440,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
             v = GATED ? act_fn<ACT>(su[e][i], sg[e][i] + b) : act_fn<ACT>(su[e][i] + b, 0.f);
           }
         }
+        over |= fp16_overflows(v);
         hv[i] = (f16)v;
       }
       u32x2 packed;
@@ -447,6 +449,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
       *reinterpret_cast<u32x2*>(h + (size_t)t * ldh + p) = packed;
     }
   }
+  raise_flag_if_any(flags, over, PI_FLAG_FP16_RANGE);
 }
 
 // ---------------------------------------------------------------------------
@@ -576,13 +579,14 @@ template <int ACT>
 __global__ __launch_bounds__(256) void k_mfin(const float* __restrict__ zp, const float* __restrict__ zg,
                                               const float* __restrict__ bias, const int32_t* __restrict__ idx,
                                               const int32_t* __restrict__ count_ptr, int max_count, int d_ff, int nt,
-                                              int ldz, f16* __restrict__ h, int ldh) {
+                                              int ldz, f16* __restrict__ h, int ldh, unsigned* __restrict__ flags) {
   constexpr bool GATED = ACT == ACT_REGLU;
   const int cnt = clamp_count(count_ptr, max_count);
   const int quads = (cnt + 63) / 64 * 16;
   const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= nt * quads) return;
-  const int t = e / quads, p = (e - t * quads) * 4;
+  const bool live = e < nt * quads;
+  if (__ballot(live) == 0ull) return;          // whole waves leave together (the flag check below is per wave)
+  const int t = live ? e / quads : 0, p = live ? (e - t * quads) * 4 : cnt;
   f32x4 u{0.f, 0.f, 0.f, 0.f}, gs{0.f, 0.f, 0.f, 0.f};
   if (p < cnt) {
 #pragma unroll
@@ -593,6 +597,7 @@ __global__ __launch_bounds__(256) void k_mfin(const float* __restrict__ zp, cons
     }
   }
   f16 hv[4];
+  bool over = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int n = p + i < cnt ? idx[p + i] : -1;
@@ -601,8 +606,11 @@ __global__ __launch_bounds__(256) void k_mfin(const float* __restrict__ zp, cons
       const float b = bias ? bias[n] : 0.f;
       v = GATED ? act_fn<ACT>(u[i], gs[i] + b) : act_fn<ACT>(u[i] + b, 0.f);
     }
+    over |= fp16_overflows(v);
     hv[i] = (f16)v;
   }
+  raise_flag_if_any(flags, over, PI_FLAG_FP16_RANGE);
+  if (!live) return;
   u32x2 packed;
   packed.x = __builtin_bit_cast(unsigned, f16x2{hv[0], hv[1]});
   packed.y = __builtin_bit_cast(unsigned, f16x2{hv[2], hv[3]});
@@ -846,16 +854,18 @@ __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, 
 // flag, adds the counts of the workgroups before it (dispatched before it, so
 // the grid needs no co-residency), and writes the marked rows' numbers at
 // their list positions in ascending order; the last workgroup writes the
-// count.  The list equals k_compact's over the same union row.  status[] is
-// zero at launch (k_tsplit clears it); every wait is bounded, so the grid
-// always drains.
+// count.  The list equals k_compact's over the same union row.  status[] and
+// *fault are zero at launch (k_tsplit clears them); every wait is bounded
+// (hdr[PI_WS_WAIT_POLLS] polls, or kDefaultWaitPolls), so the grid always
+// drains; a wait that runs out sets *fault (the merge then writes NaN) and
+// PI_FLAG_WAIT_EXPIRED in hdr[0].
 // ---------------------------------------------------------------------------
 constexpr unsigned kListReady = 0x80000000u;
-constexpr int kListSpin = 1 << 16;
 
 template <int THREADS, int R>
 __device__ void list_marked(const int* __restrict__ uni, int base, int d_ff, unsigned* __restrict__ status,
-                            int32_t* __restrict__ idx, int32_t* __restrict__ count, int* wl /* [THREADS/64] */) {
+                            int32_t* __restrict__ idx, int32_t* __restrict__ count, int* wl /* [THREADS/64] */,
+                            unsigned* __restrict__ hdr, unsigned* __restrict__ fault) {
   static_assert(R <= THREADS && R % kWave == 0, "one thread per row");
   constexpr int W = THREADS / kWave;
   const int lane = lane_id(), wave = wave_id();
@@ -872,19 +882,27 @@ __device__ void list_marked(const int* __restrict__ uni, int base, int d_ff, uns
     n_g += cw;
   }
   const int wg = blockIdx.x;
-  if (threadIdx.x == 0)
+  const unsigned polls_hook = hdr[PI_WS_WAIT_POLLS], skip_hook = hdr[PI_WS_SKIP_PUBLISH];
+  const int max_polls = polls_hook ? (int)polls_hook : kDefaultWaitPolls;
+  if (threadIdx.x == 0 && skip_hook != (unsigned)wg + 1u)
     __hip_atomic_store(&status[wg], kListReady | (unsigned)n_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int part = 0;
+  bool expired = false;
   for (int p = threadIdx.x; p < wg; p += THREADS) {
     unsigned v = __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int spin = 0; !(v & kListReady) && spin < kListSpin; ++spin) {
+    for (int spin = 0; !(v & kListReady) && spin < max_polls; ++spin) {
       __builtin_amdgcn_s_sleep(2);
       v = __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    expired |= !(v & kListReady);
     part += (int)(v & ~kListReady);
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+  if (__ballot(expired) != 0ull && lane == 0) {
+    raise_flag(fault, 1u);
+    raise_flag(hdr + PI_WS_FLAGS, PI_FLAG_WAIT_EXPIRED);
+  }
   __syncthreads();                                  // every wave has read wl[] above
   if (lane == 0) wl[wave] = part;
   __syncthreads();
@@ -899,22 +917,29 @@ __device__ void list_marked(const int* __restrict__ uni, int base, int d_ff, uns
 // k_tsplit: t = sum of the k splits of the first product in split order
 // (fp32), and its fp16 split t_hi = fp16(t), t_lo = fp16(t - t_hi), stored
 // step-major ([rank/128][nt][128]) for k_mp2.
-// It also clears zero_n words at zero_ptr (the list counters of k_mp2 /
-// k_mp2_wide in the same call); NULL skips it.
+// It also clears zero_n words at zero_ptr and the word at fault (the list
+// counters of k_mp2 / k_mp2_wide in the same call); NULL skips them.  A t_hi
+// that is not finite in fp16 raises PI_FLAG_FP16_RANGE in *flags.
 __global__ __launch_bounds__(256) void k_tsplit(const float* __restrict__ part, int n_split, int nt, int rank,
                                                 float* __restrict__ t, f16* __restrict__ th, f16* __restrict__ tl,
-                                                unsigned* __restrict__ zero_ptr, int zero_n) {
+                                                unsigned* __restrict__ zero_ptr, int zero_n,
+                                                unsigned* __restrict__ fault, unsigned* __restrict__ flags) {
   const int n = nt * rank;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (zero_ptr != nullptr && e < zero_n) zero_ptr[e] = 0u;
-  if (e >= n) return;
+  if (fault != nullptr && e == 0) *fault = 0u;
+  if (__ballot(e < n) == 0ull) return;          // whole waves leave together (the flag check below is per wave)
+  const bool live = e < n;
+  const int ee = live ? e : 0;
   float v[16];
 #pragma unroll
-  for (int sp = 0; sp < 16; ++sp) v[sp] = sp < n_split ? part[(size_t)sp * n + e] : 0.f;
+  for (int sp = 0; sp < 16; ++sp) v[sp] = sp < n_split ? part[(size_t)sp * n + ee] : 0.f;
   float sum = v[0];
 #pragma unroll
   for (int sp = 1; sp < 16; ++sp)
     if (sp < n_split) sum += v[sp];
+  raise_flag_if_any(flags, live && fp16_overflows(sum), PI_FLAG_FP16_RANGE);
+  if (!live) return;
   t[e] = sum;
   const f16 hi = (f16)sum;
   const int j = e / rank, r = e - j * rank;
@@ -929,7 +954,8 @@ __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, 
                                                     int d_ff, int nt, float theta, uint8_t* __restrict__ mask,
                                                     float* __restrict__ logits, uint8_t* __restrict__ umask,
                                                     int umask_first, unsigned* __restrict__ status,
-                                                    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+                                                    int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                                                    unsigned* __restrict__ hdr, unsigned* __restrict__ fault) {
   constexpr int NQ = kMuMB * NB;
   __shared__ float red[kMuWaves][NQ][4][kWave];
   __shared__ int uni[kMuRows];                 // union over the tile's tokens
@@ -1013,7 +1039,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, 
     }
     if (idx) {
       __syncthreads();
-      list_marked<kMuThreads, kMuRows>(uni, r0, d_ff, status, idx, count, wl);
+      list_marked<kMuThreads, kMuRows>(uni, r0, d_ff, status, idx, count, wl, hdr, fault);
     }
   }
 }
@@ -1137,7 +1163,8 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
                                                          uint8_t* __restrict__ mask, float* __restrict__ logits,
                                                          uint8_t* __restrict__ umask, int umask_first,
                                                          unsigned* __restrict__ status, int32_t* __restrict__ idx,
-                                                         int32_t* __restrict__ count) {
+                                                         int32_t* __restrict__ count, unsigned* __restrict__ hdr,
+                                                         unsigned* __restrict__ fault) {
   constexpr int LU = 16 * NB * kMuK / 8;          // 16-byte units of one step (all token slots)
   __shared__ u32x4 th_l[kMpPiece][16 * NB * kTokStride], tl_l[kMpPiece][16 * NB * kTokStride];
   __shared__ int uni[kMpRows];                    // union over the tile's tokens
@@ -1219,7 +1246,7 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
     }
     if (idx) {
       __syncthreads();
-      list_marked<kMpThreads, kMpRows>(uni, base, d_ff, status, idx, count, wl);
+      list_marked<kMpThreads, kMpRows>(uni, base, d_ff, status, idx, count, wl, hdr, fault);
     }
   }
 }
@@ -1292,7 +1319,7 @@ hipError_t launch_mup(const SparseArgs& a, const f16* x, int nt, f16* h, int ldh
     const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
     const int n = nt * (grid * kMxRows / 4);       // covers nt x (count rounded up to 64) / 4
     hipLaunchKernelGGL((k_mfin<ACT>), dim3((n + 255) / 256), dim3(256), 0, s, w.zp, w.zg, bias, a.idx, a.count,
-                       a.max_count, a.d_ff, nt, ldz, h, ldh);
+                       a.max_count, a.d_ff, nt, ldz, h, ldh, a.flags);
     return hipGetLastError();
   }
   const int rows_per_wg = 16 * mup_mb<NB>();
@@ -1301,7 +1328,7 @@ hipError_t launch_mup(const SparseArgs& a, const f16* x, int nt, f16* h, int ldh
   const float* bias = ACT == ACT_REGLU ? a.b_gate : a.b_up;
   const size_t so = std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
   hipLaunchKernelGGL((k_mup<WF, ACT, NB>), dim3(grid), dim3(kMuThreads), 0, s, a.w_up, a.w_gate, so, bias, x, a.d,
-                     a.d_ff, nt, a.idx, a.count, a.max_count, h, ldh);
+                     a.d_ff, nt, a.idx, a.count, a.max_count, h, ldh, a.flags);
   return hipGetLastError();
 }
 
@@ -1345,7 +1372,7 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t yoff = (size_t)t0 * a.d * (a.ytype == 1 ? 2 : 4);
-  return launch_merge(a.part, chunks, nt * a.d, static_cast<char*>(a.y) + yoff, a.ytype, s);
+  return launch_merge(a.part, chunks, nt * a.d, static_cast<char*>(a.y) + yoff, a.ytype, a.fault, s);
 }
 
 template <typename WF>
@@ -1376,6 +1403,8 @@ struct PredList {
   int n_status;
   int32_t* idx;
   int32_t* count;
+  unsigned* hdr;     // workspace header: flags and the wait hooks
+  unsigned* fault;   // per-call fault word of the list
 };
 
 template <int NB>
@@ -1398,23 +1427,26 @@ hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x,
   if (xs_out) *xs_out = xs;
   const int grid2 = NB >= 3 ? (d_ff + kMpRows - 1) / kMpRows : (d_ff + kMuRows - 1) / kMuRows;
   const bool list = pl.idx != nullptr && umask != nullptr;
-  if (list && (pl.status == nullptr || pl.count == nullptr || grid2 > pl.n_status)) return hipErrorInvalidValue;
+  if (list && (pl.status == nullptr || pl.count == nullptr || pl.hdr == nullptr || pl.fault == nullptr ||
+               grid2 > pl.n_status))
+    return hipErrorInvalidValue;
   const int n = nt * rank;
   const int zn = list ? grid2 : 0;
   const int nz = n > zn ? n : zn;
   hipLaunchKernelGGL(k_tsplit, dim3((nz + 255) / 256), dim3(256), 0, s, part, splits, nt, rank, t, th, tl,
-                     list ? pl.status : nullptr, zn);
+                     list ? pl.status : nullptr, zn, list ? pl.fault : nullptr, pl.hdr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   unsigned* st = list ? pl.status : nullptr;
   int32_t* li = list ? pl.idx : nullptr;
   int32_t* lc = list ? pl.count : nullptr;
+  unsigned* fl = list ? pl.fault : nullptr;
   if constexpr (NB >= 3)
     hipLaunchKernelGGL((k_mp2_wide<NB>), dim3(grid2), dim3(kMpThreads), 0, s, p2, c, th, tl, rank, d_ff, nt, theta,
-                       mask, logits, umask, first, st, li, lc);
+                       mask, logits, umask, first, st, li, lc, pl.hdr, fl);
   else
     hipLaunchKernelGGL((k_mp2<NB>), dim3(grid2), dim3(kMuThreads), 0, s, p2, c, th, tl, rank, d_ff, nt, theta, mask,
-                       logits, umask, first, st, li, lc);
+                       logits, umask, first, st, li, lc, pl.hdr, fl);
   return hipGetLastError();
 }
 
@@ -1462,12 +1494,12 @@ size_t pred_mfma_part_bytes(int d, int rank, int) {
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
                                uint8_t* umask, unsigned* status, int n_status, int32_t* idx, int32_t* count,
-                               const void** xs_out, hipStream_t s) {
+                               unsigned* hdr, unsigned* fault, const void** xs_out, hipStream_t s) {
   if (xs_out) *xs_out = nullptr;
   for (int t0 = 0; t0 < n_tok; t0 += kMfmaTile) {
     const int nt = n_tok - t0 < kMfmaTile ? n_tok - t0 : kMfmaTile;
     const bool last = t0 + nt == n_tok;
-    const PredList pl{status, n_status, last ? idx : nullptr, count};
+    const PredList pl{status, n_status, last ? idx : nullptr, count, hdr, fault};
     const f16* xs = nullptr;
     const f16* xt = static_cast<const f16*>(x) + (size_t)t0 * d;
     float* tt = t + (size_t)t0 * rank;

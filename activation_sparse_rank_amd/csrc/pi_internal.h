@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pi.h"
+
 namespace pi {
 
 // ---------------------------------------------------------------------------
@@ -86,6 +88,31 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 enum : int { ACT_RELU = 0, ACT_REGLU = 1, ACT_RELU2 = 2 };
 
 // ---------------------------------------------------------------------------
+// Fault reporting (the workspace header of pi.h).  hdr points at the header:
+// hdr[0] collects sticky flag bits, hdr[1] and hdr[2] are the test hooks of
+// the in-kernel waits.  A per-call fault word (cleared by an earlier kernel
+// of the same call) tells the merge to write NaN.
+// ---------------------------------------------------------------------------
+constexpr int kHdrWords = PI_WS_HEADER_BYTES / 4;
+constexpr int kDefaultWaitPolls = 1 << 16;
+
+__device__ __forceinline__ void raise_flag(unsigned* word, unsigned bits) {
+  if (word != nullptr) __hip_atomic_fetch_or(word, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// True when v is not finite after rounding to fp16 (the value a matrix-core
+// operand holds).
+__device__ __forceinline__ bool fp16_overflows(float v) {
+  const float r = (float)(_Float16)v;
+  return !(__builtin_fabsf(r) <= 65504.f);
+}
+
+// Raise bits in *word once per wave when any lane's cond holds.
+__device__ __forceinline__ void raise_flag_if_any(unsigned* word, bool cond, unsigned bits) {
+  if (__ballot(cond) != 0ull && (threadIdx.x & 63) == 0) raise_flag(word, bits);
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers (each returns the hipError_t of its launch)
 // ---------------------------------------------------------------------------
 
@@ -126,6 +153,11 @@ struct SparseArgs {
   // Matrix-core path, fp16 weights, one token tile: x already copied
   // step-major ([d/128][n_tok][128] fp16) by the predictor; NULL: copy it.
   const void* xs_pre = nullptr;
+  // Sticky flags word (PI_FLAG_FP16_RANGE from the matrix-core H); nullable.
+  unsigned* flags = nullptr;
+  // Per-call fault word of the list's producer; nonzero makes the merge
+  // write NaN.  NULL when the list came from no waiting kernel.
+  const unsigned* fault = nullptr;
 };
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
 
@@ -141,6 +173,8 @@ struct LayerArgs {
   unsigned* status;         // workspace [layer_segments(d_ff)], zero at launch
   int32_t* idx;             // workspace [d_ff]
   int32_t* count;           // workspace, one int
+  unsigned* hdr;            // workspace header (flags, wait hooks)
+  unsigned* fault;          // per-call fault word, zero at launch
 };
 // n_tok <= min(sparse_tile(wtype, d), pred_tile(rank)); a.idx / a.count must be L.idx / L.count.
 hipError_t launch_layer_fused(const SparseArgs& a, const LayerArgs& L, hipStream_t s);
@@ -170,13 +204,21 @@ hipError_t launch_sparse_ffn_mfma(const SparseArgs& a, hipStream_t s);
 // xs_out (nullable) receives the step-major token copy when n_tok <= 64.
 bool pred_mfma_path(int wtype, int d, int rank, int n_tok);
 size_t pred_mfma_part_bytes(int d, int rank, int n_tok);
+// hdr: the workspace header (flags; the wait hooks when listing); fault: the
+// per-call fault word of the list (cleared in the call), nullable when not
+// listing.
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
                                uint8_t* umask, unsigned* status, int n_status, int32_t* idx, int32_t* count,
-                               const void** xs_out, hipStream_t s);
+                               unsigned* hdr, unsigned* fault, const void** xs_out, hipStream_t s);
 
-// y = sum over c of part[c][0 .. n), in chunk order (fp32 or fp16 out).
-hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, hipStream_t s);
+// y = sum over c of part[c][0 .. n), in chunk order (fp32 or fp16 out); NaN
+// everywhere when fault (nullable) holds a nonzero word.
+hipError_t launch_merge(const float* part, int n_chunks, int n, void* y, int ytype, const unsigned* fault,
+                        hipStream_t s);
+
+// Zero the kHdrWords words of a workspace header (pi_clear_flags).
+hipError_t launch_clear_header(unsigned* hdr, hipStream_t s);
 
 hipError_t launch_q4_0_repack(const void* src, int rows, int cols, void* dst, hipStream_t s);
 

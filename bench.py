@@ -133,14 +133,10 @@ def _time_graph(graph, reps, stream):
     return start.elapsed_time(end) / reps          # ms per replay
 
 
-def cpu_baseline(cfg, layers, xs_host, budget_s=20.0, max_samples=64):
-    """The oracle's layer() on host copies of a few layers and tokens."""
+def _oracle_rate(cfg, layers, xs_host, budget_s):
+    """layer-tokens/s of the oracle's layer() over every (layer, step) of the
+    sample, in order, stopping early once budget_s seconds are spent."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:       # pragma: no cover - threadpoolctl missing
-        threads = os.cpu_count() or 1
     # xs_host: [steps][layers][batch][d]; one oracle call takes one step's batch of one layer
     done, calls, t_total = 0, 0, 0.0
     for li, hl in enumerate(layers):
@@ -151,19 +147,37 @@ def cpu_baseline(cfg, layers, xs_host, budget_s=20.0, max_samples=64):
             t_total += time.perf_counter() - t0
             done += x.shape[0]
             calls += 1
-            if t_total > budget_s or calls >= max_samples:
+            if t_total > budget_s:
                 break
-        if t_total > budget_s or calls >= max_samples:
+        if t_total > budget_s:
             break
+    return done / t_total, done, calls, t_total
+
+
+def cpu_baseline(cfg, layers, xs_host, budget_s=15.0):
+    """The oracle's layer() (float64 numpy) on host copies of the first layers
+    and steps of the same stack: once with the BLAS pool on every core it may
+    use, once limited to one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    affinity = len(os.sched_getaffinity(0))
+    v_all, done, calls, t_all = _oracle_rate(cfg, layers, xs_host, budget_s)
+    with threadpool_limits(limits=1):
+        v_one, done1, _, t_one = _oracle_rate(cfg, layers, xs_host, budget_s)
     return {
-        "value": done / t_total,
+        "value": round(v_all, 3),
         "unit": "layer-tokens/s",
-        "cores": threads,
+        "cores": blas,
         "kind": "oracle",
-        "sample": f"oracle layer (predict, compact, sparse FFN; float64) on {done} layer-tokens in {calls} calls "
-                  f"(layers 0-{len(layers) - 1}, steps 0-{xs_host.shape[0] - 1}, batch {xs_host.shape[2]}) "
-                  f"of the same stack, "
-                  f"{t_total:.1f} s on {os.cpu_count()} host cores ({threads} BLAS threads)",
+        "value_1_thread": round(v_one, 3),
+        "cpu_count": os.cpu_count(),
+        "affinity_cpus": affinity,
+        "blas_threads": blas,
+        "sample": f"oracle layer (predict, compact, sparse FFN; float64) on layers 0-{len(layers) - 1} x steps "
+                  f"0-{xs_host.shape[0] - 1} (batch {xs_host.shape[2]}) of the same stack: {done} layer-tokens in "
+                  f"{calls} calls, {t_all:.1f} s with {blas} BLAS threads; {done1} layer-tokens in {t_one:.1f} s "
+                  f"with 1 thread; {os.cpu_count()} host cores, {affinity} in this process's affinity mask",
     }
 
 
@@ -231,7 +245,7 @@ def _ffn_kernels(cfg, n_tok):
 def _kernels(cfg, n_tok):
     """Kernels of one pi_layer call (labels only)."""
     pred = _pred_kernels(cfg, n_tok)
-    if n_tok <= _tile(cfg) and n_tok <= 8 and pred == "k_pred1 + k_pred2":
+    if n_tok <= _tile(cfg) and pred == "k_pred1 + k_pred2" and _ffn_kernels(cfg, n_tok).startswith("k_up"):
         return f"k_pred1 + k_pred_up + {'k_down_q4' if cfg.wtype == 'q4_0' else 'k_down'} + k_merge"
     ffn = _ffn_kernels(cfg, n_tok)
     if pred.startswith("k_xstep"):
@@ -257,6 +271,7 @@ def main(argv=None):
     ap.add_argument("--no-hot-order", action="store_true",
                     help="keep the generated neuron order (default: place neurons by profiled hotness)")
     ap.add_argument("--calib", type=int, default=256, help="calibration tokens per layer for the hotness profile")
+    ap.add_argument("--repeats", type=int, default=5, help="timed runs of the step loop (median and minimum reported)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -278,7 +293,7 @@ def main(argv=None):
     xdt = torch.float16 if cfg.x_dtype == "f16" else torch.float32
     n_prompt = cfg.prompt if (B == 1 and cfg.prompt > 0 and not args.no_prompt) else 0
 
-    n_base_layers, n_base_tok = 4, 16
+    n_base_layers, n_base_tok = 2, 4
     q4 = cfg.wtype == "q4_0"
     mats = ("w_up", "w_down_t", "w_gate")
     t_gen = time.perf_counter()
@@ -308,7 +323,7 @@ def main(argv=None):
     preds = [pi.Predictor(lw["p1"], lw["p2"], lw["c"]) for lw in layers]
     ffns = [pi.FFN(lw["w_up"], lw["w_down_t"], cfg.act, b_up=lw.get("b_up"), w_gate=lw.get("w_gate"),
                    b_gate=lw.get("b_gate"), d_model=d if q4 else None) for lw in layers]
-    ws = torch.empty(pi.workspace_bytes(preds[0], ffns[0], B), dtype=torch.uint8, device=dev)
+    ws = pi.alloc_workspace(preds[0], ffns[0], B, dev)        # zero-filled: fault flags clear
     x_stage = torch.zeros((L, B, d), dtype=xdt, device=dev)
     y_all = torch.empty((L, B, d), dtype=torch.float32, device=dev)
 
@@ -332,18 +347,27 @@ def main(argv=None):
         for t in range(args.warmup):
             step(t)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        for t in range(args.warmup, T):
-            step(t)
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
+    # the timed steps, repeated: each repeat replays the same K steps
+    rep_ms = []
+    for r in range(max(1, args.repeats)):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            for t in range(args.warmup, T):
+                step(t)
+            end.record(stream)
+        torch.cuda.synchronize()
+        rep_ms.append(start.elapsed_time(end))
+        print(f"[bench] repeat {r + 1}: {args.steps} steps, {rep_ms[-1] / args.steps:.4f} ms/step", file=sys.stderr,
+              flush=True)
+    ms_total = float(np.median(rep_ms))
     ms_step = ms_total / args.steps
     layer_tok_s = args.steps * L * B / (ms_total / 1e3)
-    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+    flags_step = pi.read_flags(ws, stream)
+    if flags_step:
+        print(f"[bench] fault flags raised during the timed steps: {flags_step:#x}", file=sys.stderr, flush=True)
 
     # ---------------- per-(layer, step) list lengths of the timed steps ----------------
     mask = torch.empty((L, B, f), dtype=torch.uint8, device=dev)
@@ -425,7 +449,7 @@ def main(argv=None):
     parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if B == 1 else METRIC.replace("(batch 1)", f"(batch {B})"),
         "value": round(layer_tok_s, 1),
         "unit": "layer-tokens/s",
         "n_gpus": 1,
@@ -442,6 +466,12 @@ def main(argv=None):
                    "mean_density": cfg.rho, "parallelism": "none (1 GPU)",
                    "neuron_order": ("as generated" if args.no_hot_order else
                                     f"by hotness ({args.calib} calibration tokens per layer)")},
+        "repeats": {"n": len(rep_ms), "value": "median",
+                    "ms_per_step_median": round(ms_step, 4),
+                    "ms_per_step_min": round(min(rep_ms) / args.steps, 4),
+                    "ms_per_step_max": round(max(rep_ms) / args.steps, 4),
+                    "value_at_min": round(args.steps * L * B / (min(rep_ms) / 1e3), 1)},
+        "fault_flags": flags_step,
         "roofline": layer_roof,
         "roofline_parts": parts,
         "count_mean": round(cnt_mean, 1),

@@ -27,8 +27,9 @@
  *    are host memory, read during the call only.  The library keeps no
  *    mutable global state.
  *  - Streams: calls are asynchronous and ordered on `stream` (a hipStream_t;
- *    NULL = the default stream).  No call synchronises the host or copies
- *    device->host, so every call may be captured into a HIP graph.
+ *    NULL = the default stream).  No call but pi_read_flags synchronises
+ *    the host or copies device->host, so every other call may be captured
+ *    into a HIP graph.
  *  - Errors: arguments are validated on the host BEFORE anything is
  *    launched; on any error the call returns a status and launches nothing.
  *    A failed launch returns PI_E_HIP (pi_last_error() gives the HIP message,
@@ -38,6 +39,8 @@
  *    [n_tok][d_model].  All array pointers must be 16-byte aligned.
  *  - Determinism: identical inputs give bitwise identical outputs on every
  *    run (no atomics in any reduction; every sum has a fixed order).
+ *  - Fault flags: every workspace starts with a 256-byte header whose first
+ *    32-bit word collects PI_FLAG_* bits (see pi_read_flags).
  */
 #ifndef PI_H_
 #define PI_H_
@@ -106,6 +109,47 @@ typedef struct pi_ffn {
  * 0 for invalid descriptors.  */
 size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n_tok);
 
+/* ---- Workspace header and fault flags -----------------------------------
+ * The first PI_WS_HEADER_BYTES of every workspace are a header of 32-bit
+ * words; the sections a call uses follow it.
+ *   word PI_WS_FLAGS: sticky fault flags.  Kernels only OR PI_FLAG_* bits
+ *     into it; nothing in the library clears it except pi_clear_flags.  A
+ *     zero-filled new workspace starts with no flags.
+ *   word PI_WS_WAIT_POLLS: test hook, the bound on the polls of each
+ *     in-kernel wait for another workgroup's count (0 = the built-in bound,
+ *     65536 polls of about 128 clock cycles each).
+ *   word PI_WS_SKIP_PUBLISH: test hook, 1 + the index of one workgroup of an
+ *     in-kernel list that leaves its count unpublished, so the waits of the
+ *     workgroups after it give up (0 = none).
+ * Both hooks exist to force the give-up path from the host; leave them 0.
+ *
+ * pi_layer lists the predicted neurons inside the kernel that decides them:
+ * each workgroup publishes its count and waits, a bounded number of polls,
+ * for the counts of the workgroups with smaller indices.  That relies on the
+ * workgroups of one launch being dispatched in increasing index order (as
+ * the GPU's dispatcher does), never on co-residency.  If a wait runs out
+ * anyway, the call raises PI_FLAG_WAIT_EXPIRED and writes NaN to every
+ * element of its y, so a wrong list never passes as a result.  */
+#define PI_WS_HEADER_BYTES 256
+#define PI_WS_FLAGS 0
+#define PI_WS_WAIT_POLLS 1
+#define PI_WS_SKIP_PUBLISH 2
+#define PI_FLAG_WAIT_EXPIRED 1u /* an in-kernel wait gave up; that call's y is all NaN            */
+#define PI_FLAG_FP16_RANGE 2u   /* a value the matrix-core path keeps in fp16 (the FFN's H, or the
+                                   predictor's t) was not finite after rounding to fp16; the
+                                   affected outputs are inf or NaN                              */
+
+/* Zero the header of ws (flags and test hooks).  Asynchronous on stream, a
+ * kernel (no memset), so it may be captured into a graph.
+ * Errors: NULL ws, ws not 16-byte aligned.  */
+pi_status pi_clear_flags(void* ws, void* stream);
+
+/* Read the flags word of ws into *flags (host memory).  The one SYNCHRONOUS
+ * call of this library: it waits for the work queued on stream before it
+ * returns, so the flags of every earlier call on that stream are included.
+ * Errors: NULL pointers, ws not 16-byte aligned, PI_E_HIP.  */
+pi_status pi_read_flags(const void* ws, uint32_t* flags, void* stream);
+
 /* Predict which neurons each token activates.
  *   x:      [n_tok][d_model], dtype xtype == pred->wtype
  *   tau:    probability threshold in (0, 1); compared as l_i > ln(tau/(1-tau))
@@ -151,7 +195,9 @@ pi_status pi_sparse_ffn(const pi_ffn* ffn, const void* x, int32_t xtype, int32_t
 
 /* One layer: pi_predict, pi_compact, pi_sparse_ffn on the same x.  The
  * predictor and FFN must agree on d_model and d_ff.  Mask, list and count
- * live in ws.  Cited passage: [QB] "Общая архитектура PowerInfer".  */
+ * live in ws.  y is all NaN when the call raised PI_FLAG_WAIT_EXPIRED (see
+ * the workspace header above).  Cited passage: [QB] "Общая архитектура
+ * PowerInfer".  */
 pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int32_t xtype,
                    int32_t n_tok, float tau, void* y, int32_t ytype,
                    void* ws, size_t ws_bytes, void* stream);

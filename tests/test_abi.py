@@ -178,3 +178,19 @@ def test_stream_read_rejects(lib):
     assert lib.pi_stream_read(FAKE, 0, 0x20000, None) == L.PI_E_SHAPE
     assert lib.pi_stream_read(FAKE, 24, 0x20000, None) == L.PI_E_SHAPE
     assert lib.pi_stream_read(FAKE_ODD, 32, 0x20000, None) == L.PI_E_ALIGN
+
+
+def test_flag_calls_reject(lib):
+    assert lib.pi_clear_flags(None, None) == L.PI_E_NULL
+    assert lib.pi_clear_flags(FAKE_ODD, None) == L.PI_E_ALIGN
+    out = ctypes.c_uint32(0)
+    assert lib.pi_read_flags(None, ctypes.byref(out), None) == L.PI_E_NULL
+    assert lib.pi_read_flags(FAKE, None, None) == L.PI_E_NULL
+    assert lib.pi_read_flags(FAKE_ODD, ctypes.byref(out), None) == L.PI_E_ALIGN
+
+
+def test_workspace_has_header(lib):
+    # Every workspace starts with the PI_WS_HEADER_BYTES header: a predictor-only
+    # workspace is the header plus the section of t (and nothing else at 1 token).
+    p = _pred(d=1024, r=64, f=512)
+    assert lib.pi_workspace_bytes(ctypes.byref(p), None, 1) == L.PI_WS_HEADER_BYTES + 256

@@ -57,3 +57,4 @@ def test_layer_graph_replays_match_eager(name, n_tok):
         pi.layer(dl.pred, dl.ffn, xs[(k + 1) % 3], cfg.tau, y_e, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(y_e, refs[(k + 1) % 3])
+    assert pi.read_flags(ws) == 0, "fault flags raised"

@@ -260,8 +260,9 @@ def _layer_check(dl: DeviceLayer, n_tok: int, tokens_checked=None, stream_id=0, 
     pi.sparse_ffn(dl.ffn, x, idx, cnt, y_sep)
     # and the fused layer call
     y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
-    pi.layer(dl.pred, dl.ffn, x, cfg.tau, y)
-    torch.cuda.synchronize()
+    ws = pi.alloc_workspace(dl.pred, dl.ffn, n_tok)
+    pi.layer(dl.pred, dl.ffn, x, cfg.tau, y, ws=ws)
+    assert pi.read_flags(ws) == 0, f"{what}: fault flags raised"
     assert torch.equal(y, y_sep), f"{what}: pi_layer differs from predict+compact+sparse_ffn"
 
     h = dl.oracle_args()
@@ -298,6 +299,64 @@ def test_layer_falcon_prompt64():
     cfg = workload.get_config("falcon40b")
     dl = DeviceLayer(cfg, layer=1)
     _layer_check(dl, n_tok=64, tokens_checked=[0, 17, 63], what="falcon prompt 64")
+
+
+def test_layer_falcon_b2():
+    # The fused single-tile kernel at 2 tokens and an ordinary threshold: the
+    # union of two partly active masks is listed in-kernel.
+    cfg = workload.get_config("falcon40b")
+    dl = DeviceLayer(cfg, layer=3)
+    for s in range(2):
+        _layer_check(dl, n_tok=2, stream_id=s, what=f"falcon b2 #{s}")
+
+
+@pytest.mark.parametrize("name,n_tok,rows", [
+    ("tiny_relu2", 1, None), ("tiny_relu2", 2, None), ("tiny_relu2", 8, None),
+    ("falcon40b_relu2", 1, None), ("falcon40b_relu2", 2, None), ("falcon40b_relu2", 8, [0, 3, 7]),
+    ("falcon40b_relu2", 64, [0, 31, 63]),
+])
+def test_layer_relu2(name, n_tok, rows):
+    # Squared ReLU through pi_layer: the fused kernel (1-2 tokens; tiny fp32 up
+    # to 8) and the matrix-core path (8 and 64 fp16 tokens).
+    cfg = workload.get_config(name)
+    dl = DeviceLayer(cfg, layer=0)
+    _layer_check(dl, n_tok=n_tok, tokens_checked=rows, what=f"{name} n={n_tok}")
+
+
+@pytest.mark.parametrize("d", [1000, 1024])
+@pytest.mark.parametrize("n_tok", [3, 4, 5, 8])
+@pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
+def test_layer_rank64_tiles(d, n_tok, act):
+    # An fp16 predictor of rank 64 (not a multiple of 128: the VALU predictor
+    # at any token count).  d = 1000: the FFN has no matrix-core path either,
+    # so pi_layer runs the fused kernel on a tile of 3-8 tokens; d = 1024: the
+    # FFN takes the matrix cores and pi_layer runs the three calls.
+    f, r, tau = 2500, 64, 0.45
+    g = torch.Generator(device="cuda").manual_seed(d + 13 * n_tok + len(act))
+    p1 = (torch.randn((r, d), generator=g, device="cuda") * 0.05).half()
+    p2 = (torch.randn((f, r), generator=g, device="cuda") * 0.2).half()
+    c = (torch.randn(f, generator=g, device="cuda") * 0.5 - 1.2).float()
+    kw = rand_ffn(d, f, act, torch.float16, seed=n_tok + d)
+    pred, ffn, hk = pi.Predictor(p1, p2, c), pi.FFN(**kw), host_ffn(kw)
+    x = torch.randn((n_tok, d), generator=g, device="cuda").half()
+    mask = torch.empty((n_tok, f), dtype=torch.uint8, device="cuda")
+    pi.predict(pred, x, tau, mask)
+    idx, cnt = _i32(f), _i32(1)
+    pi.compact(mask, idx, cnt)
+    y_sep = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    pi.sparse_ffn(ffn, x, idx, cnt, y_sep)
+    y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    ws = pi.alloc_workspace(pred, ffn, n_tok)
+    pi.layer(pred, ffn, x, tau, y, ws=ws)
+    assert pi.read_flags(ws) == 0
+    assert torch.equal(y, y_sep), "pi_layer differs from predict + compact + sparse_ffn"
+    ref_l, _ = oracle.predict(host(x), host(p1), host(p2), host(c), tau)
+    check_mask(host(mask), ref_l, tau, f"rank64 n={n_tok}")
+    c_ = int(cnt.item())
+    ref_idx, ref_c = oracle.compact(host(mask))
+    assert c_ == ref_c and np.array_equal(host(idx)[:c_], ref_idx)
+    assert 0 < c_ < f
+    check_y(host(y), oracle.sparse_ffn(host(x), ref_idx, **hk), TOL["f16"], f"rank64 d={d} n={n_tok} {act}")
 
 
 @pytest.mark.parametrize("n_tok", [3, 5, 8, 20, 64, 70, 130])

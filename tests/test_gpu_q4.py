@@ -157,8 +157,9 @@ def _layer_check(dl, n_tok, rows=None, stream_id=0, what=""):
     y_sep = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
     pi.sparse_ffn(dl.ffn, x, idx, cnt, y_sep)
     y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
-    pi.layer(dl.pred, dl.ffn, x, cfg.tau, y)
-    torch.cuda.synchronize()
+    ws = pi.alloc_workspace(dl.pred, dl.ffn, n_tok)
+    pi.layer(dl.pred, dl.ffn, x, cfg.tau, y, ws=ws)
+    assert pi.read_flags(ws) == 0, f"{what}: fault flags raised"
     assert torch.equal(y, y_sep), f"{what}: pi_layer differs from predict+compact+sparse_ffn"
     h = dl.oracle_args()
     xs = host(x)
@@ -177,4 +178,6 @@ def test_layer_q4_model_shape(name):
     cfg = workload.get_config(name)
     dl = DeviceLayer(cfg, layer=0)
     _layer_check(dl, n_tok=1, what=f"{name} b1")
+    # two tokens: the fused kernel's Q4_0 tile of 2 (x of both tokens in LDS)
+    _layer_check(dl, n_tok=2, stream_id=2, what=f"{name} b2")
     _layer_check(dl, n_tok=8, rows=[0, 5, 7], stream_id=1, what=f"{name} b8")

@@ -59,6 +59,10 @@ CONFIGS = {
     "falcon40b": Config("falcon40b", 8192, 32768, 60, 1024, "f16", "relu", 0.10, prompt=64),
     # Llama2-70B ReGLU-shaped stack (gate/up/down), predictor on the gate.
     "llama70b": Config("llama70b", 8192, 28672, 80, 1024, "f16", "reglu", 0.10),
+    # Squared-ReLU variants (the pages list squared ReLU beside ReLU and ReGLU
+    # as a supported activation): the tiny fp32 case and the Falcon shape.
+    "tiny_relu2": Config("tiny_relu2", 256, 1024, 1, 32, "f32", "relu2", 0.15, n_decode=8),
+    "falcon40b_relu2": Config("falcon40b_relu2", 8192, 32768, 60, 1024, "f16", "relu2", 0.10, prompt=64),
     # Q4_0 variants of the two large shapes, batch 1 and batch 8 decode.
     "falcon40b_q4": Config("falcon40b_q4", 8192, 32768, 60, 1024, "q4_0", "relu", 0.10),
     "llama70b_q4": Config("llama70b_q4", 8192, 28672, 80, 1024, "q4_0", "reglu", 0.10),
