@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     count_active,
     hot_order,
     layer,
+    layer_noalloc,
     permute_rows,
     place_layer,
     stream_read,

@@ -22,7 +22,7 @@ STATUS_NAMES = {
 
 # Every symbol include/pi.h declares.
 EXPORTS = ("pi_workspace_bytes", "pi_clear_flags", "pi_read_flags", "pi_predict", "pi_compact", "pi_sparse_ffn",
-           "pi_layer", "pi_q4_0_repack", "pi_count_active", "pi_hot_order", "pi_permute_rows", "pi_stream_read",
+           "pi_layer", "pi_layer_noalloc", "pi_q4_0_repack", "pi_count_active", "pi_hot_order", "pi_permute_rows", "pi_stream_read",
            "pi_status_str", "pi_last_error")
 
 PI_SEGMENT_ROWS = 32   # neurons per segment of pi_layer's fused kernel (pi.h)
@@ -32,6 +32,7 @@ PI_STREAM_BLOCKS = 2048  # entries of pi_stream_read's output (pi.h)
 PI_WS_HEADER_BYTES = 256
 PI_WS_FLAGS, PI_WS_WAIT_POLLS, PI_WS_SKIP_PUBLISH = 0, 1, 2
 PI_FLAG_WAIT_EXPIRED, PI_FLAG_FP16_RANGE = 1, 2
+PI_NOALLOC_SCRATCH_BYTES = 32 << 20   # static scratch of pi_layer_noalloc (pi.h)
 
 
 class PiPredictor(ctypes.Structure):
@@ -75,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pi_sparse_ffn.restype = ctypes.c_int
     lib.pi_layer.argtypes = [PP(PiPredictor), PP(PiFFN), P, i32, i32, f32, P, i32, P, sz, P]
     lib.pi_layer.restype = ctypes.c_int
+    lib.pi_layer_noalloc.argtypes = [PP(PiPredictor), PP(PiFFN), P, i32, i32, f32, P, i32, P]
+    lib.pi_layer_noalloc.restype = ctypes.c_int
     lib.pi_q4_0_repack.argtypes = [P, i32, i32, P, P]
     lib.pi_q4_0_repack.restype = ctypes.c_int
     lib.pi_count_active.argtypes = [P, i32, i32, P, P]

@@ -20,7 +20,8 @@ class PiError(RuntimeError):
     def __init__(self, status: int, where: str):
         lib = L.load()
         msg = lib.pi_status_str(status).decode()
-        extra = lib.pi_last_error().decode() if status == L.PI_E_HIP else ""
+        detailed = status == L.PI_E_HIP or (status == L.PI_E_WORKSPACE and where == "pi_layer_noalloc")
+        extra = lib.pi_last_error().decode() if detailed else ""
         super().__init__(f"{where}: {L.STATUS_NAMES.get(status, status)} ({msg}){' ' + extra if extra else ''}")
         self.status = status
 
@@ -235,6 +236,19 @@ def layer(pred: Predictor, ffn: FFN, x, tau: float, y, ws=None, stream=None):
                            float(tau), y.data_ptr(), _DTYPES[y.dtype], ws.data_ptr(), ws.numel(),
                            _stream(stream))
     _check(st, "pi_layer")
+
+
+def layer_noalloc(pred: Predictor, ffn: FFN, x, tau: float, y, stream=None):
+    """pi_layer with the library's static scratch (pi_layer_noalloc): the
+    same result as layer(), no workspace, and nothing allocated here either.
+    Calls that overlap on one GPU race on the shared scratch."""
+    n = _x(x, ffn.d_model, ffn.x_dtype)
+    _dev(y, "y")
+    if y.dtype not in _DTYPES or y.shape != (n, ffn.d_model):
+        raise ValueError("y must be float32 or float16 [n_tok, d_model]")
+    st = L.load().pi_layer_noalloc(ctypes.byref(pred.desc), ctypes.byref(ffn.desc), x.data_ptr(), _DTYPES[x.dtype],
+                                   n, float(tau), y.data_ptr(), _DTYPES[y.dtype], _stream(stream))
+    _check(st, "pi_layer_noalloc")
 
 
 def q4_0_repack(src, rows: int, cols: int, dst=None, stream=None):

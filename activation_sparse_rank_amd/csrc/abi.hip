@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "pi.h"
@@ -164,6 +165,114 @@ pi::SparseArgs sparse_args(const pi_ffn* f, const void* x, int n_tok, const int3
   return a;
 }
 
+pi_status check_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int32_t xtype, int32_t n_tok,
+                      float tau, const void* y, int32_t ytype) {
+  pi_status st = check_pred(pred);
+  if (st != PI_OK) return st;
+  if ((st = check_ffn(ffn)) != PI_OK) return st;
+  if (pred->d_model != ffn->d_model || pred->d_ff != ffn->d_ff) return PI_E_SHAPE;
+  if (!x || !y) return PI_E_NULL;
+  if (n_tok < 1) return PI_E_SHAPE;
+  if (xtype != pred->wtype || xtype != x_type_of(ffn)) return PI_E_DTYPE;
+  if (ytype != PI_F32 && ytype != PI_F16) return PI_E_DTYPE;
+  if (!al16(x) || !al16(y)) return PI_E_ALIGN;
+  return check_tau(tau);
+}
+
+// The launch sequence of one layer on workspace w (laid out as L).
+pi_status run_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int n_tok, float tau, void* y,
+                    int ytype, char* w, const Layout& L, hipStream_t s) {
+  float* t = reinterpret_cast<float*>(w + L.t);
+  uint8_t* mask = reinterpret_cast<uint8_t*>(w + L.mask);
+  int32_t* idx = reinterpret_cast<int32_t*>(w + L.idx);
+  int32_t* count = reinterpret_cast<int32_t*>(w + L.count);
+  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
+  unsigned* fault = status + L.n_segments;
+  unsigned* hdr = reinterpret_cast<unsigned*>(w);
+  pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
+  // The fused kernel takes one token tile of the list path; where either
+  // stand-alone call would take the matrix cores, the layer does too, so that
+  // pi_layer always equals pi_predict + pi_compact + pi_sparse_ffn bit for bit.
+  const bool fused = n_tok <= pi::sparse_tile(ffn->wtype, ffn->d_model) && n_tok <= pi::pred_tile(pred->rank) &&
+                     !pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok) &&
+                     !pi::mfma_path(ffn->wtype, ffn->d_model, n_tok);
+  hipError_t e;
+  if (fused) {
+    // Stage 1 also clears the fused kernel's segment counters and the fault word after them.
+    e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, status,
+                                  L.n_segments + 1, s);
+    if (e != hipSuccess) return hip_fail(e);
+    pi::LayerArgs la;
+    la.p2 = pred->p2;
+    la.c = pred->c;
+    la.t = t;
+    la.rank = pred->rank;
+    la.theta = theta_of(tau);
+    la.status = status;
+    la.idx = idx;
+    la.count = count;
+    la.hdr = hdr;
+    la.fault = fault;
+    a.fault = fault;
+    e = pi::launch_layer_fused(a, la, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return PI_OK;
+  }
+  // Many tokens: predict every token, take the union list, then the list path.
+  if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok)) {
+    // The matrix-core predictor writes the union mask and lists it (idx,
+    // count) in its last kernel; the fp16 FFN reuses its step-major copy
+    // of a single token tile.
+    const void* xs = nullptr;
+    e = pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
+                                theta_of(tau), t, w + L.tpart, nullptr, nullptr, mask, status, L.n_segments, idx,
+                                count, hdr, fault, &xs, s);
+    a.xs_pre = xs;
+    a.fault = fault;
+  } else {
+    e = predict_any(pred, x, n_tok, theta_of(tau), t, w, L, mask, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = pi::launch_compact(mask, n_tok, ffn->d_ff, idx, count, s);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  e = pi::launch_sparse_ffn(a, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+
+// Scratch of pi_layer_noalloc: one static array per GPU, held until the
+// process ends.  Host code never uses the symbol's name as an address (on the
+// host it names a stand-in, not device memory): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current,
+// and only that pointer reaches kernels.
+static __device__ __align__(256) unsigned char scratch[PI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address; the first call on a device takes it
+// and clears the scratch's header (a kernel on s, like pi_clear_flags).
+hipError_t static_scratch(hipStream_t s, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0) return hipErrorInvalidSymbol;
+    e = pi::launch_clear_header(static_cast<unsigned*>(ptr), s);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,77 +335,29 @@ pi_status pi_sparse_ffn(const pi_ffn* ffn, const void* x, int32_t xtype, int32_t
 
 pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int32_t xtype, int32_t n_tok,
                    float tau, void* y, int32_t ytype, void* ws, size_t ws_bytes, void* stream) {
-  pi_status st = check_pred(pred);
+  pi_status st = check_layer(pred, ffn, x, xtype, n_tok, tau, y, ytype);
   if (st != PI_OK) return st;
-  if ((st = check_ffn(ffn)) != PI_OK) return st;
-  if (pred->d_model != ffn->d_model || pred->d_ff != ffn->d_ff) return PI_E_SHAPE;
-  if (!x || !y) return PI_E_NULL;
-  if (n_tok < 1) return PI_E_SHAPE;
-  if (xtype != pred->wtype || xtype != x_type_of(ffn)) return PI_E_DTYPE;
-  if (ytype != PI_F32 && ytype != PI_F16) return PI_E_DTYPE;
-  if (!al16(x) || !al16(y)) return PI_E_ALIGN;
-  if ((st = check_tau(tau)) != PI_OK) return st;
   const Layout L = layout(pred, ffn, n_tok);
   if ((st = check_ws(ws, ws_bytes, L.total)) != PI_OK) return st;
+  return run_layer(pred, ffn, x, n_tok, tau, y, ytype, static_cast<char*>(ws), L, as_stream(stream));
+}
 
-  char* w = static_cast<char*>(ws);
-  float* t = reinterpret_cast<float*>(w + L.t);
-  uint8_t* mask = reinterpret_cast<uint8_t*>(w + L.mask);
-  int32_t* idx = reinterpret_cast<int32_t*>(w + L.idx);
-  int32_t* count = reinterpret_cast<int32_t*>(w + L.count);
-  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
-  unsigned* fault = status + L.n_segments;
-  unsigned* hdr = reinterpret_cast<unsigned*>(w);
+pi_status pi_layer_noalloc(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int32_t xtype,
+                           int32_t n_tok, float tau, void* y, int32_t ytype, void* stream) {
+  pi_status st = check_layer(pred, ffn, x, xtype, n_tok, tau, y, ytype);
+  if (st != PI_OK) return st;
+  const Layout L = layout(pred, ffn, n_tok);
+  if (L.total > (size_t)PI_NOALLOC_SCRATCH_BYTES) {
+    g_last_error = "pi_layer_noalloc: this layer and token count need " + std::to_string(L.total) +
+                   " bytes of scratch; the library's static scratch holds " +
+                   std::to_string((size_t)PI_NOALLOC_SCRATCH_BYTES) + " (use pi_layer with a workspace)";
+    return PI_E_WORKSPACE;
+  }
   const hipStream_t s = as_stream(stream);
-  pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
-  // The fused kernel takes one token tile of the list path; where either
-  // stand-alone call would take the matrix cores, the layer does too, so that
-  // pi_layer always equals pi_predict + pi_compact + pi_sparse_ffn bit for bit.
-  const bool fused = n_tok <= pi::sparse_tile(ffn->wtype, ffn->d_model) && n_tok <= pi::pred_tile(pred->rank) &&
-                     !pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok) &&
-                     !pi::mfma_path(ffn->wtype, ffn->d_model, n_tok);
-  hipError_t e;
-  if (fused) {
-    // Stage 1 also clears the fused kernel's segment counters and the fault word after them.
-    e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, status,
-                                  L.n_segments + 1, s);
-    if (e != hipSuccess) return hip_fail(e);
-    pi::LayerArgs la;
-    la.p2 = pred->p2;
-    la.c = pred->c;
-    la.t = t;
-    la.rank = pred->rank;
-    la.theta = theta_of(tau);
-    la.status = status;
-    la.idx = idx;
-    la.count = count;
-    la.hdr = hdr;
-    la.fault = fault;
-    a.fault = fault;
-    e = pi::launch_layer_fused(a, la, s);
-    if (e != hipSuccess) return hip_fail(e);
-    return PI_OK;
-  }
-  // Many tokens: predict every token, take the union list, then the list path.
-  if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok)) {
-    // The matrix-core predictor writes the union mask and lists it (idx,
-    // count) in its last kernel; the fp16 FFN reuses its step-major copy
-    // of a single token tile.
-    const void* xs = nullptr;
-    e = pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
-                                theta_of(tau), t, w + L.tpart, nullptr, nullptr, mask, status, L.n_segments, idx,
-                                count, hdr, fault, &xs, s);
-    a.xs_pre = xs;
-    a.fault = fault;
-  } else {
-    e = predict_any(pred, x, n_tok, theta_of(tau), t, w, L, mask, nullptr, s);
-    if (e != hipSuccess) return hip_fail(e);
-    e = pi::launch_compact(mask, n_tok, ffn->d_ff, idx, count, s);
-  }
+  char* w = nullptr;
+  const hipError_t e = static_scratch(s, &w);
   if (e != hipSuccess) return hip_fail(e);
-  e = pi::launch_sparse_ffn(a, s);
-  if (e != hipSuccess) return hip_fail(e);
-  return PI_OK;
+  return run_layer(pred, ffn, x, n_tok, tau, y, ytype, w, L, s);
 }
 
 pi_status pi_q4_0_repack(const void* src, int32_t rows, int32_t cols, void* dst, void* stream) {

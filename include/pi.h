@@ -23,9 +23,11 @@
  * Conventions for every entry point:
  *  - Ownership: every array pointer is DEVICE memory owned by the caller.  The
  *    library allocates and frees nothing; scratch space comes from the
- *    caller's workspace `ws` (see pi_workspace_bytes).  Descriptor structs
+ *    caller's workspace `ws` (see pi_workspace_bytes), or for
+ *    pi_layer_noalloc from a static array inside the library.  Descriptor structs
  *    are host memory, read during the call only.  The library keeps no
- *    mutable global state.
+ *    mutable global state beyond the per-device address of
+ *    pi_layer_noalloc's static scratch.
  *  - Streams: calls are asynchronous and ordered on `stream` (a hipStream_t;
  *    NULL = the default stream).  No call but pi_read_flags synchronises
  *    the host or copies device->host, so every other call may be captured
@@ -202,6 +204,29 @@ pi_status pi_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, i
                    int32_t n_tok, float tau, void* y, int32_t ytype,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* ---- A layer call that allocates nothing --------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same call and result as pi_layer (bit for bit), with its
+ * scratch in a static device array of PI_NOALLOC_SCRATCH_BYTES inside the
+ * library: one per GPU, held until the process ends, its address taken once
+ * per device on the first call there (with that device current).  The call
+ * itself allocates nothing and calls no allocating routine.
+ *   x, y, descriptors, n_tok, tau, xtype, ytype, stream: as pi_layer; the
+ *   stream must belong to the current device.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that overlap on one GPU (different streams, or
+ * different host threads) race and give wrong results; order them.  Each
+ * call clears the counters it waits on itself.  The scratch's fault flags
+ * cannot be read; a call whose in-kernel wait gave up still writes NaN to y.
+ * Errors: as pi_layer; PI_E_WORKSPACE (with a pi_last_error() message) when
+ * pi_workspace_bytes(pred, ffn, n_tok) exceeds PI_NOALLOC_SCRATCH_BYTES --
+ * up to 32 tokens per call fit for fp16 layers of the Falcon-40B / Llama2-70B
+ * shapes, 16 for Q4_0.  */
+#define PI_NOALLOC_SCRATCH_BYTES (32u << 20)
+pi_status pi_layer_noalloc(const pi_predictor* pred, const pi_ffn* ffn, const void* x, int32_t xtype,
+                           int32_t n_tok, float tau, void* y, int32_t ytype, void* stream);
+
 /* Convert canonical Q4_0 blocks into the layout the kernels read.
  *   src: [rows][cols/32] blocks of 18 bytes (little-endian fp16 scale d, then
  *        16 bytes; byte j holds code j in its low nibble and code j+16 in its
@@ -275,7 +300,8 @@ pi_status pi_stream_read(const void* src, size_t bytes, uint32_t* out, void* str
 /* Static text for a status code.  */
 const char* pi_status_str(pi_status s);
 
-/* Text of the last PI_E_HIP error on this host thread ("" if none).  */
+/* Text of the last PI_E_HIP error, or of pi_layer_noalloc's PI_E_WORKSPACE,
+ * on this host thread ("" if none).  */
 const char* pi_last_error(void);
 
 #ifdef __cplusplus
