@@ -14,11 +14,13 @@ from .api import (  # noqa: F401
     compact,
     count_active,
     hot_order,
+    rank_order,
     layer,
     layer_noalloc,
     permute_rows,
     place_layer,
     stream_read,
+    gather_read,
     predict,
     q4_0_repack,
     read_flags,

@@ -22,7 +22,7 @@ STATUS_NAMES = {
 
 # Every symbol include/pi.h declares.
 EXPORTS = ("pi_workspace_bytes", "pi_clear_flags", "pi_read_flags", "pi_predict", "pi_compact", "pi_sparse_ffn",
-           "pi_layer", "pi_layer_noalloc", "pi_q4_0_repack", "pi_count_active", "pi_hot_order", "pi_permute_rows", "pi_stream_read",
+           "pi_layer", "pi_layer_noalloc", "pi_q4_0_repack", "pi_count_active", "pi_hot_order", "pi_rank_order", "pi_permute_rows", "pi_stream_read", "pi_gather_read",
            "pi_status_str", "pi_last_error")
 
 PI_SEGMENT_ROWS = 32   # neurons per segment of pi_layer's fused kernel (pi.h)
@@ -84,10 +84,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pi_count_active.restype = ctypes.c_int
     lib.pi_hot_order.argtypes = [P, i32, P]
     lib.pi_hot_order.restype = ctypes.c_int
+    lib.pi_rank_order.argtypes = [P, i32, P]
+    lib.pi_rank_order.restype = ctypes.c_int
     lib.pi_permute_rows.argtypes = [P, i32, i32, P, P, P]
     lib.pi_permute_rows.restype = ctypes.c_int
     lib.pi_stream_read.argtypes = [P, sz, P, P]
     lib.pi_stream_read.restype = ctypes.c_int
+    lib.pi_gather_read.argtypes = [P, i32, i32, P, P, i32, P, P]
+    lib.pi_gather_read.restype = ctypes.c_int
     lib.pi_status_str.argtypes = [ctypes.c_int]
     lib.pi_status_str.restype = ctypes.c_char_p
     lib.pi_last_error.argtypes = []

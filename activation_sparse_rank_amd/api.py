@@ -293,6 +293,18 @@ def hot_order(counts) -> torch.Tensor:
     return perm
 
 
+def rank_order(counts) -> torch.Tensor:
+    """Placement order by rank (pi_rank_order, host memory): perm[k] is the
+    neuron with the k-th highest count, ties by lower number."""
+    c = counts.detach().to("cpu").contiguous()
+    if c.dtype != torch.int32 or c.dim() != 1:
+        raise ValueError("counts must be int32 [d_ff]")
+    perm = torch.empty(c.numel(), dtype=torch.int32)
+    st = L.load().pi_rank_order(c.data_ptr(), c.numel(), perm.data_ptr())
+    _check(st, "pi_rank_order")
+    return perm
+
+
 def permute_rows(src, perm, dst=None, stream=None):
     """dst row k = src row perm[k] over the first dimension (pi_permute_rows)."""
     _dev(src, "src"), _dev(perm, "perm")
@@ -344,4 +356,27 @@ def stream_read(src, out=None, stream=None):
         raise ValueError("out must be int32 [PI_STREAM_BLOCKS]")
     st = L.load().pi_stream_read(src.data_ptr(), nbytes, out.data_ptr(), _stream(stream))
     _check(st, "pi_stream_read")
+    return out
+
+
+def gather_read(src, rows, count, row_bytes=None, max_count=None, out=None, stream=None):
+    """Read the listed rows of src once (pi_gather_read): rows[0 .. count) of
+    the [src.shape[0], row_bytes] matrix; returns out, whose XOR over its
+    PI_STREAM_BLOCKS int32 entries is the XOR of those rows' 32-bit words."""
+    _dev(src, "src"), _dev(rows, "rows"), _dev(count, "count")
+    n_rows = src.shape[0]
+    rb = src.numel() * src.element_size() // n_rows if row_bytes is None else int(row_bytes)
+    if rows.dtype != torch.int32 or count.dtype != torch.int32:
+        raise TypeError("rows and count must be int32")
+    mc = rows.numel() if max_count is None else int(max_count)
+    if rows.numel() < mc:
+        raise ValueError("rows is shorter than max_count")
+    if out is None:
+        out = torch.empty(L.PI_STREAM_BLOCKS, dtype=torch.int32, device=src.device)
+    _dev(out, "out")
+    if out.dtype != torch.int32 or out.numel() != L.PI_STREAM_BLOCKS:
+        raise ValueError("out must be int32 [PI_STREAM_BLOCKS]")
+    st = L.load().pi_gather_read(src.data_ptr(), n_rows, rb, rows.data_ptr(), count.data_ptr(), mc, out.data_ptr(),
+                                 _stream(stream))
+    _check(st, "pi_gather_read")
     return out

@@ -387,6 +387,13 @@ pi_status pi_hot_order(const uint32_t* counts, int32_t d_ff, int32_t* perm) {
   return PI_OK;
 }
 
+pi_status pi_rank_order(const uint32_t* counts, int32_t d_ff, int32_t* perm) {
+  if (!counts || !perm) return PI_E_NULL;
+  if (d_ff < 1) return PI_E_SHAPE;
+  pi::hot_order(counts, d_ff, 1, perm);     // dealing over segments of one row: the sorted order
+  return PI_OK;
+}
+
 pi_status pi_permute_rows(const void* src, int32_t rows, int32_t row_bytes, const int32_t* perm, void* dst,
                           void* stream) {
   if (!src || !dst || !perm) return PI_E_NULL;
@@ -424,6 +431,19 @@ pi_status pi_read_flags(const void* ws, uint32_t* flags, void* stream) {
   hipError_t e = hipMemcpyAsync(flags, static_cast<const unsigned*>(ws) + PI_WS_FLAGS, sizeof(uint32_t),
                                 hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_gather_read(const void* src, int32_t n_rows, int32_t row_bytes, const int32_t* rows,
+                         const int32_t* count, int32_t max_count, uint32_t* out, void* stream) {
+  if (!src || !rows || !count || !out) return PI_E_NULL;
+  if (n_rows < 1 || row_bytes < 16 || row_bytes % 16) return PI_E_SHAPE;
+  if (max_count < 0) return PI_E_RANGE;
+  if (!al16(src) || (reinterpret_cast<uintptr_t>(rows) & 3u) || (reinterpret_cast<uintptr_t>(count) & 3u))
+    return PI_E_ALIGN;
+  const hipError_t e =
+      pi::launch_gather_read(src, n_rows, row_bytes, rows, count, max_count, out, PI_STREAM_BLOCKS, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e);
   return PI_OK;
 }

@@ -232,5 +232,9 @@ hipError_t launch_permute_rows(const void* src, int rows, int row_bytes, const i
 // Streaming read of bytes of src by blocks workgroups; out[b] = XOR of the
 // 32-bit words workgroup b read (k_stream.hip).
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* out, int blocks, hipStream_t s);
+// Gathered read of the rows listed in rows[0 .. min(*count, max_count)) of a
+// [n_rows][row_bytes] matrix; out[b] = XOR of the words workgroup b read.
+hipError_t launch_gather_read(const void* src, int n_rows, int row_bytes, const int32_t* rows, const int32_t* count,
+                              int max_count, uint32_t* out, int blocks, hipStream_t s);
 
 }  // namespace pi

@@ -209,12 +209,14 @@ def measure_stream(pi, dev, stream, nbytes=8 << 30, reps=10):
     return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def place_by_hotness(pi, cfg, lw, layer, seed, n_cal, dev):
+def place_by_hotness(pi, cfg, lw, layer, seed, n_cal, dev, order="hot"):
     """Offline placement of one layer's neurons: run the layer's predictor on
     n_cal calibration tokens (a token stream of their own, never timed),
     count each neuron's predicted firings, and permute every per-neuron array
-    into the order pi_hot_order gives (canonical Q4_0 blocks, before the
-    repack)."""
+    into the order pi_hot_order gives ("hot": hot neurons dealt evenly over
+    the fused kernel's segments) or pi_rank_order gives ("rank": neurons by
+    firing count, the always-firing ones contiguous in the first rows);
+    canonical Q4_0 blocks are permuted before the repack."""
     import workload
 
     xc = workload.make_tokens(cfg, layer, n_cal, dev, seed, stream=2)
@@ -222,7 +224,21 @@ def place_by_hotness(pi, cfg, lw, layer, seed, n_cal, dev):
     pi.predict(pi.Predictor(lw["p1"], lw["p2"], lw["c"]), xc, cfg.tau, mask)
     counts = torch.zeros(cfg.d_ff, dtype=torch.int32, device=dev)
     pi.count_active(mask, counts)
-    return pi.place_layer(lw, pi.hot_order(counts))
+    return pi.place_layer(lw, pi.hot_order(counts) if order == "hot" else pi.rank_order(counts))
+
+
+def matrix_rows(cfg, lw, key):
+    """(tensor view, row bytes) pieces of one weight matrix whose rows a
+    gather reads: the matrix itself, or for repacked Q4_0 its code rows and
+    its scale rows."""
+    f, d = cfg.d_ff, cfg.d_model
+    w = lw[key]
+    if cfg.wtype != "q4_0":
+        return [(w, d * ELEM_BYTES[cfg.wtype])]
+    nb = d // 32
+    codes = w[:f * nb * 16].view(f, nb * 16)
+    scales = w[f * nb * 16:].view(f, nb * 2)
+    return [(codes, nb * 16)] + ([(scales, nb * 2)] if (nb * 2) % 16 == 0 else [])
 
 
 def _pred_kernels(cfg, n_tok):
@@ -269,11 +285,15 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prompt", action="store_true", help="skip the multi-token prompt measurement")
     ap.add_argument("--no-hot-order", action="store_true",
-                    help="keep the generated neuron order (default: place neurons by profiled hotness)")
+                    help="keep the generated neuron order (same as --order none)")
+    ap.add_argument("--order", choices=("hot", "rank", "none"), default="hot",
+                    help="neuron placement from the calibration profile: hot neurons dealt over the fused kernel's "
+                         "segments (hot), neurons by firing rank (rank), or the generated order (none)")
     ap.add_argument("--calib", type=int, default=256, help="calibration tokens per layer for the hotness profile")
     ap.add_argument("--repeats", type=int, default=5, help="timed runs of the step loop (median and minimum reported)")
     args = ap.parse_args(argv)
 
+    order = "none" if args.no_hot_order else args.order
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the sparse FFN is not sharded across GPUs "
               "(run with --gpus 1)", file=sys.stderr)
@@ -301,8 +321,8 @@ def main(argv=None):
     for li in range(L):
         lw = workload.make_layer(cfg, li, dev, args.seed)
         lw.pop("p")
-        if not args.no_hot_order:
-            lw = place_by_hotness(pi, cfg, lw, li, args.seed, args.calib, dev)
+        if order != "none":
+            lw = place_by_hotness(pi, cfg, lw, li, args.seed, args.calib, dev, order)
         if q4:
             # the kernels read the repacked layout; the oracle reads canonical blocks
             if li < n_base_layers and not args.no_cpu_baseline:
@@ -402,10 +422,21 @@ def main(argv=None):
     with torch.cuda.graph(g_sp, stream=stream):
         for li in range(L):
             pi.sparse_ffn(ffns[li], x_stage[li], idx[li], cnt[li:li + 1], y_all[li], ws=ws_s)
+    # the gather ceiling: the same active rows of every weight matrix read
+    # with no arithmetic (pi_gather_read), over the same lists
+    g_gr = torch.cuda.CUDAGraph()
+    gr_out = torch.empty(pi._lib.PI_STREAM_BLOCKS, dtype=torch.int32, device=dev)
+    mat_keys = [k for k in ("w_up", "w_gate", "w_down_t") if k in layers[0]]
+    with torch.cuda.graph(g_gr, stream=stream):
+        for li in range(L):
+            for k in mat_keys:
+                for view, rb in matrix_rows(cfg, layers[li], k):
+                    pi.gather_read(view, idx[li], cnt[li:li + 1], row_bytes=rb, max_count=f, out=gr_out)
     with torch.cuda.stream(stream):
         ms_pred = _time_graph(g_pred, args.reps, stream) / L
         ms_comp = _time_graph(g_comp, args.reps, stream) / L
         ms_sp = _time_graph(g_sp, args.reps, stream) / L
+        ms_gr = _time_graph(g_gr, args.reps, stream) / L
     last_cnt = cnt.cpu().numpy().astype(np.int64)
     b_pred = bytes_predict(cfg, B)
     b_comp = float(np.mean([bytes_compact(cfg, c, B) for c in last_cnt]))
@@ -442,11 +473,17 @@ def main(argv=None):
                     "bytes_per_launch": int(b_comp)},
         "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, B)})", b_sp, ms_sp),
     }
+    gather_read_gbps = round(b_act / (ms_gr * 1e-3) / 1e9, 1)
     for r in (layer_roof, parts["predict"], parts["gather"]):
         r["stream_read_gbps"] = stream_gbps
         r["frac_of_stream_read"] = round(r["achieved"] / stream_gbps, 4)
+        r["gather_read_gbps"] = gather_read_gbps
     parts["gather"]["active_weight_gbps"] = round(b_act / (ms_sp * 1e-3) / 1e9, 1)
     parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    parts["gather"]["frac_of_gather_read"] = round(parts["gather"]["active_weight_gbps"] / gather_read_gbps, 4)
+    parts["gather_read"] = {"what": "pi_gather_read of the same active rows of every weight matrix, no arithmetic",
+                            "avg_us_per_layer": round(ms_gr * 1e3, 3), "bytes_per_layer": int(b_act),
+                            "gbps": gather_read_gbps}
 
     out = {
         "metric": METRIC if B == 1 else METRIC.replace("(batch 1)", f"(batch {B})"),
@@ -464,8 +501,10 @@ def main(argv=None):
         "config": {"workload": f"{cfg.name} decode batch {B}", "d_model": d, "d_ff": f, "layers": L,
                    "rank": cfg.rank, "act": cfg.act, "weights": cfg.wtype, "batch": B,
                    "mean_density": cfg.rho, "parallelism": "none (1 GPU)",
-                   "neuron_order": ("as generated" if args.no_hot_order else
-                                    f"by hotness ({args.calib} calibration tokens per layer)")},
+                   "neuron_order": {"none": "as generated",
+                                    "hot": f"by hotness, dealt over segments ({args.calib} calibration tokens "
+                                           f"per layer)",
+                                    "rank": f"by firing rank ({args.calib} calibration tokens per layer)"}[order]},
         "repeats": {"n": len(rep_ms), "value": "median",
                     "ms_per_step_median": round(ms_step, 4),
                     "ms_per_step_min": round(min(rep_ms) / args.steps, 4),

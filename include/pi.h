@@ -270,6 +270,13 @@ pi_status pi_count_active(const uint8_t* mask, int32_t n_tok, int32_t d_ff, uint
  * Errors: NULL pointers, d_ff < 1.  */
 pi_status pi_hot_order(const uint32_t* counts, int32_t d_ff, int32_t* perm);
 
+/* Placement order by rank: perm[k] = the neuron with the k-th highest count
+ * (ties: lower neuron number first), so the always-firing neurons take the
+ * first rows, contiguous.  HOST memory, synchronous, no device work.  The
+ * alternative to pi_hot_order's dealing, for locality of the hot rows rather
+ * than balance over segments.  Errors: NULL pointers, d_ff < 1.  */
+pi_status pi_rank_order(const uint32_t* counts, int32_t d_ff, int32_t* perm);
+
 /* Row permutation: dst row k = src row perm[k], k < rows.
  *   src, dst: rows * row_bytes bytes each, device, must not overlap;
  *             16-byte aligned
@@ -296,6 +303,22 @@ pi_status pi_permute_rows(const void* src, int32_t rows, int32_t row_bytes, cons
  * Errors: NULL pointers, bytes 0 or not a multiple of 16, misaligned src.  */
 #define PI_STREAM_BLOCKS 2048
 pi_status pi_stream_read(const void* src, size_t bytes, uint32_t* out, void* stream);
+
+/* The same read restricted to listed rows: the rows rows[0 .. n) of a
+ * [n_rows][row_bytes] matrix, n = min(*count, max_count), each read whole
+ * (one wave per row, 16-byte loads), in list order across the grid.  This
+ * is the access pattern of the sparse FFN's weight gathers without their
+ * arithmetic, the ceiling such a gather can reach.
+ *   src:   n_rows * row_bytes bytes, device, 16-byte aligned
+ *   rows:  device int32 list (at least max_count entries readable); an
+ *          entry outside [0, n_rows) reads nothing
+ *   count: device int32
+ *   out:   [PI_STREAM_BLOCKS] u32, device; the XOR over out[] is the XOR of
+ *          every 32-bit word of the listed rows (a row listed twice cancels)
+ * Errors: NULL pointers, n_rows < 1, row_bytes not a positive multiple of
+ * 16, max_count < 0, misaligned pointers.  */
+pi_status pi_gather_read(const void* src, int32_t n_rows, int32_t row_bytes, const int32_t* rows,
+                         const int32_t* count, int32_t max_count, uint32_t* out, void* stream);
 
 /* Static text for a status code.  */
 const char* pi_status_str(pi_status s);

@@ -194,3 +194,11 @@ def test_workspace_has_header(lib):
     # workspace is the header plus the section of t (and nothing else at 1 token).
     p = _pred(d=1024, r=64, f=512)
     assert lib.pi_workspace_bytes(ctypes.byref(p), None, 1) == L.PI_WS_HEADER_BYTES + 256
+
+
+def test_gather_read_rejects(lib):
+    assert lib.pi_gather_read(None, 4, 16, FAKE, FAKE, 4, FAKE, None) == L.PI_E_NULL
+    assert lib.pi_gather_read(FAKE, 0, 16, FAKE, FAKE, 4, FAKE, None) == L.PI_E_SHAPE
+    assert lib.pi_gather_read(FAKE, 4, 24, FAKE, FAKE, 4, FAKE, None) == L.PI_E_SHAPE
+    assert lib.pi_gather_read(FAKE, 4, 16, FAKE, FAKE, -1, FAKE, None) == L.PI_E_RANGE
+    assert lib.pi_gather_read(FAKE_ODD, 4, 16, FAKE, FAKE, 4, FAKE, None) == L.PI_E_ALIGN

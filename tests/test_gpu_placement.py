@@ -124,3 +124,23 @@ def test_stream_read_reads_every_word(nbytes):
     got = np.bitwise_xor.reduce(host(out).view(np.uint32))
     ref = np.bitwise_xor.reduce(host(buf).view(np.uint32))
     assert got == ref
+
+
+@pytest.mark.parametrize("n_rows,row_bytes,n_list", [(100, 16, 37), (3000, 16384, 400), (777, 4608, 777)])
+def test_gather_read_reads_listed_rows(n_rows, row_bytes, n_list):
+    # The XOR over out[] equals the XOR of every 32-bit word of the listed
+    # rows (computed on the host); entries past the count and outside the
+    # matrix read nothing.
+    g = torch.Generator(device="cuda").manual_seed(n_rows)
+    src = torch.randint(0, 256, (n_rows, row_bytes), dtype=torch.uint8, device="cuda", generator=g)
+    rows_np = np.random.default_rng(n_rows).choice(n_rows, size=n_list, replace=False).astype(np.int32)
+    rows_np[::9] = -5                                   # outside the matrix: skipped
+    pad = np.full(16, 2 ** 30, dtype=np.int32)          # past the count: never read
+    rows = torch.as_tensor(np.concatenate([rows_np, pad]), device="cuda")
+    cnt = torch.tensor([n_list], dtype=torch.int32, device="cuda")
+    out = pi.gather_read(src, rows, cnt, max_count=n_list + 16)
+    host_src = src.cpu().numpy().view(np.uint32)
+    valid = rows_np[rows_np >= 0]
+    ref = np.bitwise_xor.reduce(host_src[valid].reshape(-1)) if valid.size else np.uint32(0)
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == ref

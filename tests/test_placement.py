@@ -88,3 +88,15 @@ def test_oracle_layer_invariant_under_renaming():
         assert sorted(perm[moved["idx"]].tolist()) == base["idx"].tolist()
         scale = np.abs(base["y"]).max()
         assert np.abs(moved["y"] - base["y"]).max() <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("d_ff", [1, 7, 33, 3000])
+def test_rank_order_rule(d_ff):
+    # pi_rank_order: neurons by count, highest first, ties by lower number.
+    rng = np.random.default_rng(d_ff + 1)
+    counts = rng.integers(0, 4, d_ff).astype(np.uint32)
+    lib = L.load()
+    c = np.ascontiguousarray(counts)
+    perm = np.empty(d_ff, dtype=np.int32)
+    assert lib.pi_rank_order(c.ctypes.data_as(ctypes.c_void_p), d_ff, perm.ctypes.data_as(ctypes.c_void_p)) == L.PI_OK
+    assert perm.tolist() == sorted(range(d_ff), key=lambda i: (-int(counts[i]), i))
