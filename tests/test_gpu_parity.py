@@ -50,6 +50,23 @@ def test_compact_bitexact(d_ff, n_tok):
         assert np.array_equal(host(idx)[:c], ref_idx)
 
 
+@pytest.mark.parametrize("d_ff", [65536, 98320])
+@pytest.mark.parametrize("n_tok", [17, 64])
+def test_compact_many_tiles(d_ff, n_tok):
+    # 16-byte aligned rows: one workgroup per 4096-neuron tile, each counting
+    # the tiles before it itself (up to 24 of them, 64 token rows).
+    g = torch.Generator(device="cuda").manual_seed(d_ff + n_tok)
+    for density in (0.0, 0.004, 0.05, 1.0):
+        mask = (torch.rand((n_tok, d_ff), generator=g, device="cuda") < density).to(torch.uint8)
+        idx = torch.full((d_ff,), -7, dtype=torch.int32, device="cuda")
+        cnt = _i32(1)
+        pi.compact(mask, idx, cnt)
+        ref_idx, ref_cnt = oracle.compact(host(mask))
+        c = int(cnt.item())
+        assert c == ref_cnt
+        assert np.array_equal(host(idx)[:c], ref_idx)
+
+
 def test_compact_unaligned_rows():
     # d_ff not a multiple of 16: rows of the mask are not 16-byte aligned.
     d_ff, n_tok = 1001, 5
