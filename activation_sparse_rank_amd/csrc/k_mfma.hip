@@ -212,6 +212,57 @@ struct RowStep<Q4, MB> {
   }
 };
 
+// The same step of MB 16-row blocks of fp16 rows, loaded the way a gather
+// streams fastest: 16 lanes per row, 256 contiguous bytes of one row per 16
+// lanes, so one load instruction covers 4 rows (measured on gathered 16 KB
+// rows: 6.4 TB/s, against 4.8 TB/s for the 16 rows x 64 bytes per
+// instruction of the operand layout itself).  The units are then moved into
+// the operand layout -- row l%16, sub-step s, k = 32s + 8(l/16), the natural
+// order above, so the products are the same bits -- through a wave-private
+// LDS buffer of 16 rows x kTStride units (one unit of padding per row keeps
+// the 16 rows of an operand read on different banks).
+constexpr int kTStride = kMuK / 8 + 1;
+
+template <int MB>
+struct RowStepT {
+  u32x4 v[MB][4];        // v[mb][i]: row 4i + l/16 of block mb, unit l%16 of the step
+  __device__ __forceinline__ void load(const f16* w, const int (&rowt)[MB][4], const bool (&rvt)[MB][4], int d, int kb,
+                                       int lane) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* p = reinterpret_cast<const char*>(w + (size_t)rowt[mb][i] * d + kb) + 16 * (lane & 15);
+        v[mb][i] = rvt[mb][i] ? ld_nt(p) : u32x4{0, 0, 0, 0};
+      }
+  }
+  // Operands of block mb (a[s] for sub-step s), through buf (this wave's).
+  __device__ __forceinline__ void operands(int mb, u32x4* buf, int lane, u32x4 (&a)[4]) const {
+    const int q = lane >> 4, u = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[(4 * i + q) * kTStride + u] = v[mb][i];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // the writes land before any lane reads
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = buf[u * kTStride + 4 * s + q];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // and the reads before the next block's writes
+  }
+};
+
+// Row indices of the transposed load: position 4i + l/16 of each block, from
+// the lane that holds it in the operand layout (position l%16).
+template <int MB>
+__device__ __forceinline__ void rows_for_load(const int (&row)[MB], const bool (&rv)[MB], int lane, int (&rowt)[MB][4],
+                                              bool (&rvt)[MB][4]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int src = 4 * i + (lane >> 4);
+      rowt[mb][i] = __shfl(row[mb], src, kWave);
+      rvt[mb][i] = __shfl(rv[mb] ? 1 : 0, src, kWave) != 0;
+    }
+}
+
 // NB 16-token blocks of fp16 activations for step st, from a step-major
 // copy xs[step][token][128] (see k_xstep): one step's operands of all tokens
 // are one contiguous block, so the many workgroups reading them at once
@@ -294,7 +345,9 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   constexpr int MB = mup_mb<NB>();
   constexpr int NQ = MB * NB;              // accumulator quads per lane
   constexpr int QT = quads_per_thread<NQ>();
+  constexpr bool TR = std::is_same<WF, f16>::value && !GATED;   // transposed row loads (RowStepT)
   __shared__ float red[kMuWaves][NQ][4][kWave];
+  __shared__ u32x4 w_l[TR ? kMuWaves : 1][TR ? 16 * kTStride : 1];
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -323,14 +376,22 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
 
   const int ns = d / kMuK;
   const int s0 = wave * ns / kMuWaves, s1 = (wave + 1) * ns / kMuWaves;
+  int rowt[MB][4];
+  bool rvt[MB][4];
+  if constexpr (TR) rows_for_load<MB>(row, rv, lane, rowt, rvt);
+  u32x4* wbuf = &w_l[TR ? wave : 0][0];
+  using Rows = typename std::conditional<TR, RowStepT<MB>, RowStep<WF, MB>>::type;
   struct Step {
-    RowStep<WF, MB> up;
+    Rows up;
     RowStep<WF, GATED ? MB : 1> gate;
     TokStep<NB> x;
   };
   auto load = [&](Step& S, int st) {
     const int kb = st * kMuK;
-    S.up.load(w_up, scale_off, row, rv, d, kb, g);
+    if constexpr (TR)
+      S.up.load(static_cast<const f16*>(w_up), rowt, rvt, d, kb, lane);
+    else
+      S.up.load(w_up, scale_off, row, rv, d, kb, g);
     if constexpr (GATED) S.gate.load(w_gate, scale_off, row, rv, d, kb, g);
     S.x.load(x, nt, st, g, n16);
   };
@@ -338,7 +399,10 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       u32x4 a[4], ga[4];
-      S.up.operands(mb, a);
+      if constexpr (TR)
+        S.up.operands(mb, wbuf, lane, a);
+      else
+        S.up.operands(mb, a);
       if constexpr (GATED) S.gate.operands(mb, ga);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -472,7 +536,10 @@ constexpr int kMxWaves = kMxThreads / kWave;
 constexpr int kMxMB = 2;                          // 16-row blocks per wave
 constexpr int kMxRows = kMxWaves * 16 * kMxMB;    // 256 list positions per workgroup
 constexpr int kMxSplit = 2;
-constexpr int kMxPiece = 8;                       // k steps per staged piece of x
+// k steps per staged piece of x: transposed fp16 row loads also need 8 waves x
+// 4.25 KB of LDS (RowStepT)
+template <typename WF>
+constexpr int mx_piece() { return std::is_same<WF, Q4>::value ? 8 : 4; }
 
 template <typename WF, int ACT, int NB>
 __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict__ w_up, const void* __restrict__ w_gate,
@@ -481,8 +548,13 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
                                                          const int32_t* __restrict__ count_ptr, int max_count,
                                                          float* __restrict__ zp, float* __restrict__ zg, int ldz) {
   constexpr bool GATED = ACT == ACT_REGLU;
+  // fp16 rows are loaded transposed (RowStepT); with the gate as well that
+  // would exceed the register budget, so ReGLU keeps the operand-layout loads
+  constexpr bool F16 = std::is_same<WF, f16>::value && !GATED;
+  constexpr int kMxPiece = F16 ? mx_piece<WF>() : 8;
   constexpr int LU = 16 * NB * kMuK / 8;          // 16-byte units of one step of x (all token slots)
   __shared__ u32x4 x_l[kMxPiece][16 * NB * kTokStride];
+  __shared__ u32x4 w_l[F16 ? kMxWaves : 1][F16 ? 16 * kTStride : 1];   // transposed loads (fp16 rows)
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -509,13 +581,24 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
   const int ns = d / kMuK;
   const int split = blockIdx.y;
   const int s0 = split * ns / kMxSplit, s1 = (split + 1) * ns / kMxSplit;
+  int rowt[kMxMB][4];
+  bool rvt[kMxMB][4];
+  if constexpr (F16) rows_for_load<kMxMB>(row, rv, lane, rowt, rvt);
+  u32x4* wbuf = &w_l[F16 ? wave : 0][0];
+  using Rows = typename std::conditional<F16, RowStepT<kMxMB>, RowStep<WF, kMxMB>>::type;
+  using GRows = typename std::conditional<F16, RowStepT<GATED ? kMxMB : 1>, RowStep<WF, GATED ? kMxMB : 1>>::type;
   struct Step {
-    RowStep<WF, kMxMB> up;
-    RowStep<WF, GATED ? kMxMB : 1> gate;
+    Rows up;
+    GRows gate;
   };
   auto load = [&](Step& S, int st) {
-    S.up.load(w_up, scale_off, row, rv, d, st * kMuK, g);
-    if constexpr (GATED) S.gate.load(w_gate, scale_off, row, rv, d, st * kMuK, g);
+    if constexpr (F16) {
+      S.up.load(static_cast<const f16*>(w_up), rowt, rvt, d, st * kMuK, lane);
+      if constexpr (GATED) S.gate.load(static_cast<const f16*>(w_gate), rowt, rvt, d, st * kMuK, lane);
+    } else {
+      S.up.load(w_up, scale_off, row, rv, d, st * kMuK, g);
+      if constexpr (GATED) S.gate.load(w_gate, scale_off, row, rv, d, st * kMuK, g);
+    }
   };
   for (int p0 = s0; p0 < s1; p0 += kMxPiece) {
     const int np = s1 - p0 < kMxPiece ? s1 - p0 : kMxPiece;
@@ -535,8 +618,13 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
       u32x4 a[kMxMB][4], ga[GATED ? kMxMB : 1][4];
 #pragma unroll
       for (int mb = 0; mb < kMxMB; ++mb) {
-        cur.up.operands(mb, a[mb]);
-        if constexpr (GATED) cur.gate.operands(mb, ga[mb]);
+        if constexpr (F16) {
+          cur.up.operands(mb, wbuf, lane, a[mb]);
+          if constexpr (GATED) cur.gate.operands(mb, wbuf, lane, ga[mb]);
+        } else {
+          cur.up.operands(mb, a[mb]);
+          if constexpr (GATED) cur.gate.operands(mb, ga[mb]);
+        }
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {

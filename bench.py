@@ -553,6 +553,15 @@ def main(argv=None):
             ms_ml = _time_graph(g_ml, reps, stream) / L
             ms_mp = _time_graph(g_mp, reps, stream) / L
             ms_ms = _time_graph(g_ms, reps, stream) / L
+        # the union's rows of every weight matrix read with no arithmetic
+        g_mgr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_mgr, stream=stream):
+            for li in range(L):
+                for k in mat_keys:
+                    for view, rb in matrix_rows(cfg, layers[li], k):
+                        pi.gather_read(view, idx_m[li], cnt_m[li:li + 1], row_bytes=rb, max_count=f, out=gr_out)
+        with torch.cuda.stream(stream):
+            ms_mgr = _time_graph(g_mgr, reps, stream) / L
         uc = cnt_m.cpu().numpy().astype(np.int64)
         b_ml = float(np.mean([bytes_layer(cfg, c, n) for c in uc]))
         b_ms = float(np.mean([bytes_gather(cfg, c, n) for c in uc]))
@@ -569,6 +578,11 @@ def main(argv=None):
             "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, n)})", b_ms, ms_ms),
             "gather_mfma": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                             "frac": round(tflops / 2500.0, 4), "flops_per_launch": fl},
+            "gather_read": {"what": "pi_gather_read of the union's rows of every weight matrix, no arithmetic",
+                            "avg_us_per_layer": round(ms_mgr * 1e3, 3),
+                            "bytes_per_layer": int(np.mean([bytes_active(cfg, c) for c in uc])),
+                            "gbps": round(float(np.mean([bytes_active(cfg, c) for c in uc])) / (ms_mgr * 1e-3) / 1e9,
+                                          1)},
         }
         print(f"[bench] prompt {n}: layer {ms_ml * 1e3:.1f} us, gather {ms_ms * 1e3:.1f} us", file=sys.stderr,
               flush=True)
