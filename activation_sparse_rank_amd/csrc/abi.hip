@@ -190,17 +190,18 @@ pi_status run_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, 
   unsigned* fault = status + L.n_segments;
   unsigned* hdr = reinterpret_cast<unsigned*>(w);
   pi::SparseArgs a = sparse_args(ffn, x, n_tok, idx, count, ffn->d_ff, y, ytype, w, L);
-  // The fused kernel takes one token tile of the list path; where either
-  // stand-alone call would take the matrix cores, the layer does too, so that
-  // pi_layer always equals pi_predict + pi_compact + pi_sparse_ffn bit for bit.
+  // The fused path takes one token tile of the list path; where either
+  // stand-alone call would take the matrix cores, the layer does too.  Off the
+  // fused path pi_layer equals pi_predict + pi_compact + pi_sparse_ffn bit for
+  // bit; on it the up rows and H are the same, but the down projection walks
+  // per-neuron slots in neuron ranges instead of list pieces, so y differs
+  // from the separate calls by the order of its fp32 sums only.
   const bool fused = n_tok <= pi::sparse_tile(ffn->wtype, ffn->d_model) && n_tok <= pi::pred_tile(pred->rank) &&
                      !pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok) &&
                      !pi::mfma_path(ffn->wtype, ffn->d_model, n_tok);
   hipError_t e;
   if (fused) {
-    // Stage 1 also clears the fused kernel's segment counters and the fault word after them.
-    e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, status,
-                                  L.n_segments + 1, s);
+    e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, nullptr, 0, s);
     if (e != hipSuccess) return hip_fail(e);
     pi::LayerArgs la;
     la.p2 = pred->p2;
@@ -208,12 +209,7 @@ pi_status run_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, 
     la.t = t;
     la.rank = pred->rank;
     la.theta = theta_of(tau);
-    la.status = status;
-    la.idx = idx;
-    la.count = count;
-    la.hdr = hdr;
-    la.fault = fault;
-    a.fault = fault;
+    la.act = idx;            // the list section holds the per-neuron slots
     e = pi::launch_layer_fused(a, la, s);
     if (e != hipSuccess) return hip_fail(e);
     return PI_OK;

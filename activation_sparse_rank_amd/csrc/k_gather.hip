@@ -254,37 +254,24 @@ __global__ __launch_bounds__(kUpThreads) void k_up(const void* __restrict__ w_up
 }
 
 // ---------------------------------------------------------------------------
-// k_pred_up: layer path.  Predictor stage 2, up projection and compaction
-// fused.  Workgroup g owns kPURows consecutive neurons:
+// k_pred_up: layer path.  Predictor stage 2 and the up projection fused.
+// Workgroup g owns kPURows consecutive neurons (a segment):
 //   A. every 16-lane group computes the logits of kPUSub neurons exactly as
 //      the stand-alone predictor does (their p2 loads go out before t and x
 //      are staged); a neuron is active when any token of the tile predicts it;
-//   B. the workgroup publishes its active count n_g as one atomic word that
-//      carries its own ready flag (no fence is needed: the word is the whole
-//      message);
 //   C. the active neurons are dealt round-robin to the 4 waves, each running
 //      the up projection of its share (x read from LDS); results stay in LDS;
-//   D. the workgroup sums the counts of workgroups 0 .. g-1 (published long
-//      before, in their phase B) to get its offset in the list, and writes
-//      its neurons and their h there in ascending order; the last workgroup
-//      writes the total count.
-// A workgroup only waits on workgroups with smaller indices, which are
-// dispatched before it, so the grid needs no co-residency.  The list equals
-// pi_compact's (ascending neuron numbers) and h is stored by list position,
-// so the down projection sees the same inputs on both paths.
-// status[] and *fault must be zero at launch (the first predictor stage
-// clears them).  Every wait is bounded (hdr[PI_WS_WAIT_POLLS] polls, or
-// kDefaultWaitPolls), so the grid always drains; a wait that runs out sets
-// *fault (the merge then writes NaN) and PI_FLAG_WAIT_EXPIRED in hdr[0].
+//   D. the segment's per-neuron slots are written: act[i] = i for an active
+//      neuron and -1 otherwise, h[j][i] its value (0 when inactive).
+// The slots are the list in place: the down projection takes whole segments
+// per chunk and compacts their active neurons itself (k_down's slot form),
+// so no workgroup waits on another and nothing is counted across the grid.
 // ---------------------------------------------------------------------------
 constexpr int kPUThreads = 256;
 constexpr int kPUWaves = kPUThreads / kWave;
 constexpr int kPUSub = 2;                                             // neurons per group
 constexpr int kPURows = kPUThreads / kP2Group * kPUSub;               // 32 neurons per workgroup
 static_assert(kPURows == PI_SEGMENT_ROWS, "the segment size pi_hot_order deals neurons over");
-constexpr int kPULoads = 8;                                           // status loads per thread per batch
-constexpr unsigned kReady = 0x80000000u;
-constexpr int kExpiredBit = 0x40000000;                                // > any count (d_ff < 2^30)
 // Rows per phase-C batch (ReLU; ReGLU half as many).  A fp16 row part is 64
 // bytes per lane, a Q4_0 row part 18: Q4_0 batches hold 3x as many rows in
 // the same registers, so a segment with many active neurons needs fewer
@@ -298,17 +285,14 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
                                                         float theta, const void* __restrict__ w_up,
                                                         const void* __restrict__ w_gate, size_t scale_off,
                                                         const float* __restrict__ bias, const W* __restrict__ x,
-                                                        int d, int nt, unsigned* __restrict__ status,
-                                                        int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                                                        float* __restrict__ h, unsigned* __restrict__ hdr,
-                                                        unsigned* __restrict__ fault) {
+                                                        int d, int nt, int32_t* __restrict__ act,
+                                                        float* __restrict__ h) {
   extern __shared__ float smem[];    // t tile [NT][rank], then (XL) x tile [NT][d/E] chunks
   float* t_lds = smem;
   u32x4* x_lds = reinterpret_cast<u32x4*>(smem + NT * rank);
   __shared__ int act_lds[kPURows];
   __shared__ float pu_lds[kPUWaves][kPURows][NT];                     // part sums of phase C
   __shared__ float pg_lds[ACT == ACT_REGLU ? kPUWaves : 1][kPURows][NT];
-  __shared__ int red_lds[kPUWaves];       // phase D: per-wave count sums, kExpiredBit if a wait ran out
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane & (kP2Group - 1);
@@ -316,8 +300,6 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   const int wg = blockIdx.x;
   const int seg0 = wg * kPURows;
   const char* xb = reinterpret_cast<const char*>(x);
-  const unsigned polls_hook = hdr[PI_WS_WAIT_POLLS], skip_hook = hdr[PI_WS_SKIP_PUBLISH];
-  const int max_polls = polls_hook ? (int)polls_hook : kDefaultWaitPolls;
 
   // ---- A: logits ----
   int rows[kPUSub];
@@ -349,11 +331,6 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   }
   __syncthreads();
   const unsigned long long am = __ballot(lane < kPURows && act_lds[lane < kPURows ? lane : 0] != 0);
-  const int n_g = __builtin_popcountll(am);
-
-  // ---- B: publish this workgroup's count ----
-  if (threadIdx.x == 0 && skip_hook != (unsigned)wg + 1u)
-    __hip_atomic_store(&status[wg], kReady | (unsigned)n_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- C: up projection of the active neurons: wave q computes part q of
   // every active row, pu_batch rows at a time with all their loads in flight.
@@ -386,77 +363,92 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
     }
   }
 
-  // ---- D: offset = sum of the earlier workgroups' counts; write the list ----
-  // Each thread reads its share of status[0 .. wg-1] kPULoads at a time, all
-  // loads of a batch in flight together.
-  int part = 0;
-  bool expired = false;
-  for (int p0 = 0; p0 < wg; p0 += kPUThreads * kPULoads) {
-    unsigned v[kPULoads];
+  // ---- D: the segment's slots ----
+  __syncthreads();   // the part sums of phase C are in LDS
+  if (wave == 0 && lane < kPURows && seg0 + lane < d_ff) {
+    const int i = seg0 + lane;
+    const bool mine = (am >> lane) & 1ull;
+    act[i] = mine ? i : -1;
+    const float b = mine && bias ? bias[i] : 0.f;
 #pragma unroll
-    for (int u = 0; u < kPULoads; ++u) {
-      const int p = p0 + u * kPUThreads + (int)threadIdx.x;
-      v[u] = p < wg ? __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kReady;
-    }
-#pragma unroll
-    for (int u = 0; u < kPULoads; ++u) {
-      const int p = p0 + u * kPUThreads + (int)threadIdx.x;
-      for (int spin = 0; !(v[u] & kReady) && spin < max_polls; ++spin) {
-        __builtin_amdgcn_s_sleep(2);
-        v[u] = __hip_atomic_load(&status[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      expired |= !(v[u] & kReady);
-      part += (int)(v[u] & ~kReady);
-    }
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
-  const bool wave_expired = __ballot(expired) != 0ull;
-  if (lane == 0) red_lds[wave] = part | (wave_expired ? kExpiredBit : 0);
-  __syncthreads();   // also orders the part sums of phase C before their reads below
-  int off = 0, any_expired = 0;
-#pragma unroll
-  for (int w = 0; w < kPUWaves; ++w) {
-    off += red_lds[w] & ~kExpiredBit;
-    any_expired |= red_lds[w] & kExpiredBit;
-  }
-  if (any_expired && threadIdx.x == 0) {
-    raise_flag(fault, 1u);
-    raise_flag(hdr + PI_WS_FLAGS, PI_FLAG_WAIT_EXPIRED);
-  }
-  if (wave == 0) {
-    const bool mine = lane < kPURows && ((am >> lane) & 1ull);
-    const int pos = off + __builtin_popcountll(am & ((1ull << lane) - 1ull));
-    if (mine) {
-      const int i = seg0 + lane;
-      idx[pos] = i;
-      const float b = bias ? bias[i] : 0.f;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if (j < nt) {
-          const bool gt = ACT == ACT_REGLU;
-          const float g0 = gt ? pg_lds[0][lane][j] : 0.f, g1 = gt ? pg_lds[1][lane][j] : 0.f;
-          const float g2 = gt ? pg_lds[2][lane][j] : 0.f, g3 = gt ? pg_lds[3][lane][j] : 0.f;
-          h[(size_t)j * d_ff + pos] = combine_parts<ACT>(pu_lds[0][lane][j], pu_lds[1][lane][j], pu_lds[2][lane][j],
-                                                         pu_lds[3][lane][j], g0, g1, g2, g3, b);
-        }
+    for (int j = 0; j < NT; ++j) {
+      if (j < nt) {
+        const bool gt = ACT == ACT_REGLU;
+        const float g0 = gt ? pg_lds[0][lane][j] : 0.f, g1 = gt ? pg_lds[1][lane][j] : 0.f;
+        const float g2 = gt ? pg_lds[2][lane][j] : 0.f, g3 = gt ? pg_lds[3][lane][j] : 0.f;
+        h[(size_t)j * d_ff + i] = mine ? combine_parts<ACT>(pu_lds[0][lane][j], pu_lds[1][lane][j],
+                                                            pu_lds[2][lane][j], pu_lds[3][lane][j], g0, g1, g2, g3, b)
+                                       : 0.f;
       }
     }
-    if (wg == (int)gridDim.x - 1 && lane == 0) *count = off + n_g;
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_down: part[c][j][col] = sum over list positions k of chunk c (in order)
-// of h[j][k] * w_down_t[idx[k]][col].  Chunk c covers positions
-// [c*cnt/C, (c+1)*cnt/C): equal shares of the active rows.  The chunk's list
-// entries and h values are staged in LDS (up to kDnPiece at a time) so the
-// row loop issues its weight loads with no dependent global load before them.
+// k_down: part[c][j][col] = sum over the rows of chunk c (in list order) of
+// h[j][row] * w_down_t[row][col].  Two forms:
+//  * list (pi_sparse_ffn): chunk c covers list positions [c*cnt/C,
+//    (c+1)*cnt/C), equal shares of the active rows; h is by list position.
+//  * slots (pi_layer's fused path): chunk c covers the neurons of segments
+//    [c*S/C, (c+1)*S/C), whose per-neuron slots (act[i] = i or -1, h by
+//    neuron) the fused kernel wrote; the chunk's active neurons are compacted
+//    here, in ascending order, with no count needed beforehand, so the slots
+//    and the weights are two round trips, not three.
+// Either way the chunk's rows and h values are staged in LDS so the row loop
+// issues its weight loads with no dependent global load before them.
 // ---------------------------------------------------------------------------
 constexpr int kDnThreads = 512;
 constexpr int kDnWaves = kDnThreads / kWave;
 constexpr int kDnUnroll = 8;                 // rows in flight per wave
-constexpr int kDnPiece = kDnThreads;         // list entries staged per round
+constexpr int kDnPiece = kDnThreads;         // list entries staged per round (list form)
+constexpr int kDnSlots = 2 * kDnThreads;     // neurons staged per round (slot form)
+
+// Slot form: the active neurons among [nb0, min(nb0 + kDnSlots, n1)), in
+// ascending order, into rows_l / h_l; returns how many.  Thread t takes
+// neurons nb0 + 2t and nb0 + 2t + 1 (their act and h loads in one round
+// trip); offsets from a wave scan and the wave totals.
+template <int NT, int CAP>
+__device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, const float* __restrict__ h, int d_ff,
+                                           int nb0, int n1, int nt, int* rows_l, float (*h_l)[CAP], int* wsum) {
+  const int lane = lane_id(), wave = wave_id();
+  const int i0 = nb0 + 2 * (int)threadIdx.x, i1 = i0 + 1;
+  const int a0 = i0 < n1 ? act[i0] : -1, a1 = i1 < n1 ? act[i1] : -1;
+  float h0[NT], h1[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    h0[j] = j < nt && i0 < n1 ? h[(size_t)j * d_ff + i0] : 0.f;
+    h1[j] = j < nt && i1 < n1 ? h[(size_t)j * d_ff + i1] : 0.f;
+  }
+  const bool v0 = (unsigned)a0 < (unsigned)d_ff, v1 = (unsigned)a1 < (unsigned)d_ff;
+  const int c = (v0 ? 1 : 0) + (v1 ? 1 : 0);
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int pos = incl - c, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kDnWaves; ++w) {
+    pos += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  if (v0) {
+    rows_l[pos] = a0;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) h_l[j][pos] = h0[j];
+    ++pos;
+  }
+  if (v1) {
+    rows_l[pos] = a1;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) h_l[j][pos] = h1[j];
+  }
+  __syncthreads();
+  return tot;
+}
 
 template <typename W>
 __device__ __forceinline__ void axpy_chunk(float* acc, float hv, u32x4 w);
@@ -478,27 +470,38 @@ __device__ __forceinline__ void axpy_chunk<float>(float* acc, float hv, u32x4 w)
   acc[3] = __builtin_fmaf(hv, as_f(w.w), acc[3]);
 }
 
-template <typename W, int NT>
+template <typename W, int NT, bool SLOTS>
 __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt, int d, int d_ff,
                                                      const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ count_ptr, int max_count,
                                                      const float* __restrict__ h, int nt, int n_chunks,
                                                      float* __restrict__ part) {
+  // SLOTS: idx is act[d_ff], h is [nt][d_ff] by neuron, count_ptr unused
   constexpr int E = 16 / sizeof(W);
   constexpr int SW = kWave * E;               // columns per slice
+  constexpr int CAP = SLOTS ? kDnSlots : kDnPiece;
   __shared__ float red[kDnWaves][SW];
-  __shared__ int rows_l[kDnPiece];
-  __shared__ float h_l[NT][kDnPiece];
+  __shared__ int rows_l[CAP];
+  __shared__ float h_l[NT][CAP];
+  __shared__ int wsum[kDnWaves];
   const int lane = lane_id();
   const int wave = wave_id();
   const int slice = blockIdx.x;
   const int c = blockIdx.y;
   const int col = slice * SW + lane * E;
   const bool cv = col < d;
-  int cnt = *count_ptr;
-  cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
-  const int k0 = (int)(((long long)c * cnt) / n_chunks);
-  const int k1 = (int)(((long long)(c + 1) * cnt) / n_chunks);
+  int k0, k1;
+  if constexpr (SLOTS) {
+    const int n_seg = (d_ff + PI_SEGMENT_ROWS - 1) / PI_SEGMENT_ROWS;
+    k0 = PI_SEGMENT_ROWS * (int)(((long long)c * n_seg) / n_chunks);
+    const int e1 = PI_SEGMENT_ROWS * (int)(((long long)(c + 1) * n_seg) / n_chunks);
+    k1 = e1 < d_ff ? e1 : d_ff;
+  } else {
+    int cnt = *count_ptr;
+    cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
+    k0 = (int)(((long long)c * cnt) / n_chunks);
+    k1 = (int)(((long long)(c + 1) * cnt) / n_chunks);
+  }
 
   float acc[NT][E];
 #pragma unroll
@@ -507,16 +510,21 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
     for (int e = 0; e < E; ++e) acc[j][e] = 0.f;
 
   const char* base = reinterpret_cast<const char*>(w_dt) + (size_t)col * sizeof(W);
-  for (int pb = k0; pb < k1; pb += kDnPiece) {
-    const int n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
-    if ((int)threadIdx.x < n) {
-      const int i = idx[pb + threadIdx.x];
-      rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
+  for (int pb = k0; pb < k1; pb += CAP) {
+    int n;
+    if constexpr (SLOTS) {
+      n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum);
+    } else {
+      n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
+      if ((int)threadIdx.x < n) {
+        const int i = idx[pb + threadIdx.x];
+        rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
+        for (int j = 0; j < NT; ++j)
+          if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
+      }
+      __syncthreads();
     }
-    __syncthreads();
     for (int jb = wave; jb < n; jb += kDnWaves * kDnUnroll) {
       u32x4 v[kDnUnroll];
       int rows[kDnUnroll];
@@ -572,15 +580,17 @@ constexpr int kDqUnroll = 16;               // rows in flight per wave
 constexpr int kDqCols = 16;                 // columns per lane
 constexpr int kDqSW = kWave * kDqCols;      // 1024 columns per slice
 
-template <int NT>
+template <int NT, bool SLOTS>
 __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restrict__ w_dt, size_t scale_off, int d,
                                                         int d_ff, const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ count_ptr, int max_count,
                                                         const float* __restrict__ h, int nt, int n_chunks,
                                                         float* __restrict__ part) {
+  constexpr int CAP = SLOTS ? kDnSlots : kDnPiece;
   __shared__ float red[kDnWaves][kWave * 8];
-  __shared__ int rows_l[kDnPiece];
-  __shared__ float h_l[NT][kDnPiece];
+  __shared__ int rows_l[CAP];
+  __shared__ float h_l[NT][CAP];
+  __shared__ int wsum[kDnWaves];
   const int lane = lane_id();
   const int wave = wave_id();
   const int slice = blockIdx.x;
@@ -591,10 +601,18 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
   const int blk = col / 32, half = (col / 16) & 1;
   const uint8_t* code_base = w_dt + (size_t)blk * 16 + half * 8;
   const f16* scale_base = reinterpret_cast<const f16*>(w_dt + scale_off) + blk;
-  int cnt = *count_ptr;
-  cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
-  const int k0 = (int)(((long long)c * cnt) / n_chunks);
-  const int k1 = (int)(((long long)(c + 1) * cnt) / n_chunks);
+  int k0, k1;
+  if constexpr (SLOTS) {
+    const int n_seg = (d_ff + PI_SEGMENT_ROWS - 1) / PI_SEGMENT_ROWS;
+    k0 = PI_SEGMENT_ROWS * (int)(((long long)c * n_seg) / n_chunks);
+    const int e1 = PI_SEGMENT_ROWS * (int)(((long long)(c + 1) * n_seg) / n_chunks);
+    k1 = e1 < d_ff ? e1 : d_ff;
+  } else {
+    int cnt = *count_ptr;
+    cnt = cnt < 0 ? 0 : (cnt < max_count ? cnt : max_count);
+    k0 = (int)(((long long)c * cnt) / n_chunks);
+    k1 = (int)(((long long)(c + 1) * cnt) / n_chunks);
+  }
 
   float acc[NT][kDqCols];
 #pragma unroll
@@ -602,16 +620,21 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
 #pragma unroll
     for (int e = 0; e < kDqCols; ++e) acc[j][e] = 0.f;
 
-  for (int pb = k0; pb < k1; pb += kDnPiece) {
-    const int n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
-    if ((int)threadIdx.x < n) {
-      const int i = idx[pb + threadIdx.x];
-      rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
+  for (int pb = k0; pb < k1; pb += CAP) {
+    int n;
+    if constexpr (SLOTS) {
+      n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum);
+    } else {
+      n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
+      if ((int)threadIdx.x < n) {
+        const int i = idx[pb + threadIdx.x];
+        rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
+        for (int j = 0; j < NT; ++j)
+          if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
+      }
+      __syncthreads();
     }
-    __syncthreads();
     for (int jb = wave; jb < n; jb += kDnWaves * kDqUnroll) {
       u32x2 v[kDqUnroll];
       float dsc[kDqUnroll];
@@ -736,16 +759,22 @@ size_t scale_offset(const SparseArgs& a) {
   return std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
 }
 
-template <typename WF, int NT>
-hipError_t launch_down(const SparseArgs& a, void* y, int nt, hipStream_t s) {
+// slots: the fused layer path's per-neuron slots (k_pred_up) instead of a list
+template <typename WF, int NT, bool SLOTS>
+hipError_t launch_down_form(const SparseArgs& a, int nt, hipStream_t s) {
   const dim3 grid(a.n_slices, a.n_chunks);
   if constexpr (std::is_same<WF, Q4>::value)
-    hipLaunchKernelGGL((k_down_q4<NT>), grid, dim3(kDnThreads), 0, s, static_cast<const uint8_t*>(a.w_down_t),
+    hipLaunchKernelGGL((k_down_q4<NT, SLOTS>), grid, dim3(kDnThreads), 0, s, static_cast<const uint8_t*>(a.w_down_t),
                        scale_offset<WF>(a), a.d, a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
   else
-    hipLaunchKernelGGL((k_down<WF, NT>), grid, dim3(kDnThreads), 0, s, static_cast<const WF*>(a.w_down_t), a.d,
+    hipLaunchKernelGGL((k_down<WF, NT, SLOTS>), grid, dim3(kDnThreads), 0, s, static_cast<const WF*>(a.w_down_t), a.d,
                        a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <typename WF, int NT>
+hipError_t launch_down(const SparseArgs& a, bool slots, void* y, int nt, hipStream_t s) {
+  hipError_t e = slots ? launch_down_form<WF, NT, true>(a, nt, s) : launch_down_form<WF, NT, false>(a, nt, s);
   if (e != hipSuccess) return e;
   return launch_merge(a.part, a.n_chunks, nt * a.d, y, a.ytype, a.fault, s);
 }
@@ -786,12 +815,10 @@ hipError_t launch_pred_up(const SparseArgs& a, const LayerArgs& L, const typenam
   if (x_in_lds<X>(NT, a.d)) {
     const size_t lds = lds_t + (size_t)NT * a.d * sizeof(X);
     hipLaunchKernelGGL((k_pred_up<X, WF, ACT, NT, true>), dim3(grid), dim3(kPUThreads), lds, s, p2, L.c, L.t, L.rank,
-                       a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.status, L.idx, L.count, a.h,
-                       L.hdr, L.fault);
+                       a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.act, a.h);
   } else {
     hipLaunchKernelGGL((k_pred_up<X, WF, ACT, NT, false>), dim3(grid), dim3(kPUThreads), lds_t, s, p2, L.c, L.t,
-                       L.rank, a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.status, L.idx, L.count,
-                       a.h, L.hdr, L.fault);
+                       L.rank, a.d_ff, L.theta, a.w_up, a.w_gate, so, bias, x, a.d, nt, L.act, a.h);
   }
   return hipGetLastError();
 }
@@ -821,7 +848,7 @@ hipError_t run_tile(const SparseArgs& a, const LayerArgs* L, int t0, int nt, hip
   hipError_t e = up_dispatch<WF, NT>(a, L ? &Lt : nullptr, x, nt, s);
   if (e != hipSuccess) return e;
   const size_t yoff = (size_t)t0 * a.d * (a.ytype == 1 ? 2 : 4);
-  return launch_down<WF, NT>(a, static_cast<char*>(a.y) + yoff, nt, s);
+  return launch_down<WF, NT>(a, L != nullptr, static_cast<char*>(a.y) + yoff, nt, s);
 }
 
 template <typename WF>

@@ -162,21 +162,19 @@ struct SparseArgs {
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
 
 // Predictor operands of the fused layer path (one token tile): stage 2 of
-// the predictor, the compaction and the up projection run as one kernel
-// that writes the list (idx, count) the down projection reads.
+// the predictor and the up projection run as one kernel that writes
+// per-neuron slots -- act[i] = i for an active neuron, else -1, and h by
+// neuron -- which the down projection reads in its slot form.
 struct LayerArgs {
   const void* p2;
   const float* c;
   const float* t;           // [n_tok][rank] from stage 1
   int rank;
   float theta;
-  unsigned* status;         // workspace [layer_segments(d_ff)], zero at launch
-  int32_t* idx;             // workspace [d_ff]
-  int32_t* count;           // workspace, one int
-  unsigned* hdr;            // workspace header (flags, wait hooks)
-  unsigned* fault;          // per-call fault word, zero at launch
+  int32_t* act;             // workspace [d_ff]
 };
-// n_tok <= min(sparse_tile(wtype, d), pred_tile(rank)); a.idx / a.count must be L.idx / L.count.
+// n_tok <= min(sparse_tile(wtype, d), pred_tile(rank)); a.idx must be L.act and
+// a.h the slots' h ([n_tok][d_ff], by neuron).
 hipError_t launch_layer_fused(const SparseArgs& a, const LayerArgs& L, hipStream_t s);
 // Number of neuron segments (workgroups) of the fused kernel.
 int layer_segments(int d_ff);

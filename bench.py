@@ -236,8 +236,9 @@ def matrix_rows(cfg, lw, key):
     if cfg.wtype != "q4_0":
         return [(w, d * ELEM_BYTES[cfg.wtype])]
     nb = d // 32
-    codes = w[:f * nb * 16].view(f, nb * 16)
-    scales = w[f * nb * 16:].view(f, nb * 2)
+    flat = w.reshape(-1)
+    codes = flat[:f * nb * 16].view(f, nb * 16)
+    scales = flat[f * nb * 16:].view(f, nb * 2)
     return [(codes, nb * 16)] + ([(scales, nb * 2)] if (nb * 2) % 16 == 0 else [])
 
 

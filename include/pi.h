@@ -125,13 +125,17 @@ size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n
  *     workgroups after it give up (0 = none).
  * Both hooks exist to force the give-up path from the host; leave them 0.
  *
- * pi_layer lists the predicted neurons inside the kernel that decides them:
- * each workgroup publishes its count and waits, a bounded number of polls,
- * for the counts of the workgroups with smaller indices.  That relies on the
- * workgroups of one launch being dispatched in increasing index order (as
- * the GPU's dispatcher does), never on co-residency.  If a wait runs out
- * anyway, the call raises PI_FLAG_WAIT_EXPIRED and writes NaN to every
- * element of its y, so a wrong list never passes as a result.  */
+ * With one or two tokens pi_layer needs no list: the kernel that decides a
+ * neuron writes a per-neuron slot (its index, or -1), and the down
+ * projection compacts slots in LDS; nothing waits.  Where pi_layer takes the
+ * matrix cores (many tokens), the predictor's last kernel lists the union of
+ * the predicted neurons itself: each workgroup publishes its count and waits,
+ * a bounded number of polls, for the counts of the workgroups with smaller
+ * indices.  That relies on the workgroups of one launch being dispatched in
+ * increasing index order (as the GPU's dispatcher does), never on
+ * co-residency.  If a wait runs out anyway, the call raises
+ * PI_FLAG_WAIT_EXPIRED and writes NaN to every element of its y, so a wrong
+ * list never passes as a result.  */
 #define PI_WS_HEADER_BYTES 256
 #define PI_WS_FLAGS 0
 #define PI_WS_WAIT_POLLS 1

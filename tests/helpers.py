@@ -126,3 +126,36 @@ def rand_ffn(d, f, act, dtype, device="cuda", seed=0, with_bias=True):
 
 def host_ffn(kw):
     return {k: (host(v) if isinstance(v, torch.Tensor) else v) for k, v in kw.items()}
+
+
+def layer_is_fused(wtype: str, d: int, rank: int, n_tok: int) -> bool:
+    """Whether pi_layer takes its fused single-tile path for these shapes (the
+    dispatch rule the library documents): one token tile of the list path
+    (8 tokens; Q4_0: x tile within 32 KB) within one predictor tile (t of
+    the tile within 64 KB), where neither stand-alone call would use the
+    matrix cores (fp16 / Q4_0 rows with d % 128 == 0 beyond 2 fp16 tokens or
+    one Q4_0 tile; an fp16 predictor with d and rank multiples of 128 beyond
+    2 tokens)."""
+    tile = 8
+    if wtype == "q4_0":
+        while tile > 1 and tile * d * 2 > 32768:
+            tile //= 2
+    ptile = 8
+    while ptile > 1 and ptile * rank > 16384:
+        ptile //= 2
+    pred_wtype = "f16" if wtype == "q4_0" else wtype
+    pred_mfma = pred_wtype == "f16" and d % 128 == 0 and rank % 128 == 0 and n_tok > 2
+    ffn_mfma = wtype in ("f16", "q4_0") and d % 128 == 0 and n_tok > (2 if wtype == "f16" else tile)
+    return n_tok <= tile and n_tok <= ptile and not pred_mfma and not ffn_mfma
+
+
+def check_layer_vs_calls(y: torch.Tensor, y_sep: torch.Tensor, fused: bool, what=""):
+    """pi_layer against pi_predict + pi_compact + pi_sparse_ffn on the same
+    input.  Off the fused path both run the same kernels on the same list:
+    identical bits.  The fused path groups the down projection's chunks by
+    segments of neurons instead of list positions, so its fp32 sums are
+    added in another order: equal to about 1e-6 of max|y|."""
+    if not fused:
+        assert torch.equal(y, y_sep), f"{what}: pi_layer differs from predict+compact+sparse_ffn"
+        return
+    check_y(host(y), host(y_sep).astype(np.float64), 1e-5, f"{what}: pi_layer vs predict+compact+sparse_ffn")

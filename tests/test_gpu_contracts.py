@@ -8,7 +8,7 @@
     host through the workspace's test hooks, so every kernel still exits
     normally) raises PI_FLAG_WAIT_EXPIRED and makes y all NaN; a value of the
     matrix-core path that leaves the fp16 range raises PI_FLAG_FP16_RANGE;
-    ordinary calls raise nothing;
+    ordinary calls raise nothing; the fused single-tile path has no waits;
   * a call given a stream and no workspace allocates its temporary workspace
     on that stream.
 
@@ -130,24 +130,30 @@ def _set_hooks(ws, polls, skip):
     w[L.PI_WS_SKIP_PUBLISH] = skip
 
 
-@pytest.mark.parametrize("wtype,n_tok", [("f16", 1), ("f16", 2), ("q4_0", 1), ("f16", 8), ("f16", 40)])
-def test_wait_expiry_is_reported(wtype, n_tok):
-    # One workgroup of the in-kernel list leaves its count unpublished and the
-    # waits are bounded to 4 polls: every later workgroup gives up.  The call
-    # must raise PI_FLAG_WAIT_EXPIRED and write NaN to all of y; after the
-    # flags are cleared, the same call gives the normal result again.
-    # n_tok 1-2: the fused kernel (fp16 and Q4_0 rows); 8 and 40: the
-    # matrix-core predictor's list (then k_mup / k_mup_wide).
-    d, r, f, tau = 1024, 128, 4096, 0.45
-    p1, p2, c = _predictor(d, r, f, seed=77 + n_tok)
+def _expiry_layer(wtype, n_tok, seed):
+    d, r, f = 1024, 128, 4096
+    p1, p2, c = _predictor(d, r, f, seed=seed)
     pred = pi.Predictor(p1, p2, c)
     if wtype == "q4_0":
         ffn, _ = _q4_ffn(d, f, seed=5)
     else:
         ffn = pi.FFN(**rand_ffn(d, f, "relu", torch.float16, seed=8))
     x = torch.randn((n_tok, d), device="cuda").half()
+    return pred, ffn, x
+
+
+@pytest.mark.parametrize("n_tok", [8, 40])
+def test_wait_expiry_is_reported(n_tok):
+    # The matrix-core predictor lists the union in-kernel: one workgroup of
+    # that list leaves its count unpublished and the waits are bounded to 4
+    # polls, so every later workgroup gives up.  The call must raise
+    # PI_FLAG_WAIT_EXPIRED and write NaN to all of y; after the flags are
+    # cleared, the same call gives the normal result again.  (8 tokens: then
+    # k_mup; 40: k_mup_wide.)
+    tau = 0.45
+    pred, ffn, x = _expiry_layer("f16", n_tok, seed=77 + n_tok)
     ws = pi.alloc_workspace(pred, ffn, n_tok)
-    y_ok = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    y_ok = torch.empty((n_tok, x.shape[1]), dtype=torch.float32, device="cuda")
     pi.layer(pred, ffn, x, tau, y_ok, ws=ws)
     assert pi.read_flags(ws) == 0
     assert torch.isfinite(y_ok).all()
@@ -165,6 +171,23 @@ def test_wait_expiry_is_reported(wtype, n_tok):
     assert pi.read_flags(ws) & L.PI_FLAG_WAIT_EXPIRED
     assert torch.equal(y, y_ok)
     pi.clear_flags(ws)
+    pi.layer(pred, ffn, x, tau, y, ws=ws)
+    assert pi.read_flags(ws) == 0
+    assert torch.equal(y, y_ok)
+
+
+@pytest.mark.parametrize("wtype,n_tok", [("f16", 1), ("f16", 2), ("q4_0", 1)])
+def test_fused_layer_never_waits(wtype, n_tok):
+    # The fused single-tile path writes per-neuron slots and no workgroup
+    # waits on another: the wait hooks change nothing, y stays bitwise the
+    # same and no flag is raised.
+    tau = 0.45
+    pred, ffn, x = _expiry_layer(wtype, n_tok, seed=91 + n_tok)
+    ws = pi.alloc_workspace(pred, ffn, n_tok)
+    y_ok = torch.empty((n_tok, x.shape[1]), dtype=torch.float32, device="cuda")
+    pi.layer(pred, ffn, x, tau, y_ok, ws=ws)
+    _set_hooks(ws, polls=4, skip=1 + 9)
+    y = torch.full_like(y_ok, float("nan"))
     pi.layer(pred, ffn, x, tau, y, ws=ws)
     assert pi.read_flags(ws) == 0
     assert torch.equal(y, y_ok)

@@ -13,8 +13,8 @@ import torch
 import activation_sparse_rank_amd as pi
 import oracle
 import workload
-from helpers import (TOL, DeviceLayer, check_mask, check_y, host, host_ffn, oracle_sparse_chunked, rand_ffn,
-                     require_gpu, wtag)
+from helpers import (TOL, DeviceLayer, check_layer_vs_calls, check_mask, check_y, host, host_ffn, layer_is_fused,
+                     oracle_sparse_chunked, rand_ffn, require_gpu, wtag)
 
 pytestmark = pytest.mark.gpu
 
@@ -280,7 +280,7 @@ def _layer_check(dl: DeviceLayer, n_tok: int, tokens_checked=None, stream_id=0, 
     ws = pi.alloc_workspace(dl.pred, dl.ffn, n_tok)
     pi.layer(dl.pred, dl.ffn, x, cfg.tau, y, ws=ws)
     assert pi.read_flags(ws) == 0, f"{what}: fault flags raised"
-    assert torch.equal(y, y_sep), f"{what}: pi_layer differs from predict+compact+sparse_ffn"
+    check_layer_vs_calls(y, y_sep, layer_is_fused(cfg.wtype, d, cfg.rank, n_tok), what)
 
     h = dl.oracle_args()
     xs = host(x)
@@ -366,7 +366,7 @@ def test_layer_rank64_tiles(d, n_tok, act):
     ws = pi.alloc_workspace(pred, ffn, n_tok)
     pi.layer(pred, ffn, x, tau, y, ws=ws)
     assert pi.read_flags(ws) == 0
-    assert torch.equal(y, y_sep), "pi_layer differs from predict + compact + sparse_ffn"
+    check_layer_vs_calls(y, y_sep, layer_is_fused("f16", d, r, n_tok), f"rank64 d={d} n={n_tok}")
     ref_l, _ = oracle.predict(host(x), host(p1), host(p2), host(c), tau)
     check_mask(host(mask), ref_l, tau, f"rank64 n={n_tok}")
     c_ = int(cnt.item())

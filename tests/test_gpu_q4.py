@@ -13,7 +13,8 @@ import torch
 import activation_sparse_rank_amd as pi
 import oracle
 import workload
-from helpers import TOL, DeviceLayer, check_mask, check_y, host, oracle_sparse_chunked, require_gpu
+from helpers import (TOL, DeviceLayer, check_layer_vs_calls, check_mask, check_y, host, layer_is_fused,
+                     oracle_sparse_chunked, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -160,7 +161,7 @@ def _layer_check(dl, n_tok, rows=None, stream_id=0, what=""):
     ws = pi.alloc_workspace(dl.pred, dl.ffn, n_tok)
     pi.layer(dl.pred, dl.ffn, x, cfg.tau, y, ws=ws)
     assert pi.read_flags(ws) == 0, f"{what}: fault flags raised"
-    assert torch.equal(y, y_sep), f"{what}: pi_layer differs from predict+compact+sparse_ffn"
+    check_layer_vs_calls(y, y_sep, layer_is_fused(cfg.wtype, d, cfg.rank, n_tok), what)
     h = dl.oracle_args()
     xs = host(x)
     ref_l, _ = oracle.predict(xs, h["p1"], h["p2"], h["c"], cfg.tau)
