@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     gather_read,
     predict,
     q4_0_repack,
+    read_down_rows,
     read_flags,
     sparse_ffn,
     workspace_bytes,

@@ -152,7 +152,8 @@ def _temp_workspace(pred, ffn, n_tok, device, stream):
 
 
 def clear_flags(ws, stream=None):
-    """Zero the workspace header: fault flags and test hooks (pi_clear_flags)."""
+    """Zero the workspace header: fault flags, test hooks and the count of
+    down-projection rows read (pi_clear_flags)."""
     _dev(ws, "ws")
     _check(L.load().pi_clear_flags(ws.data_ptr(), _stream(stream)), "pi_clear_flags")
 
@@ -163,6 +164,16 @@ def read_flags(ws, stream=None) -> int:
     _dev(ws, "ws")
     out = ctypes.c_uint32(0)
     _check(L.load().pi_read_flags(ws.data_ptr(), ctypes.byref(out), _stream(stream)), "pi_read_flags")
+    return int(out.value)
+
+
+def read_down_rows(ws, stream=None) -> int:
+    """How many w_down_t rows the down projections of the calls on ws have
+    read, summed over calls, after the work queued on stream
+    (pi_read_down_rows; synchronises that stream)."""
+    _dev(ws, "ws")
+    out = ctypes.c_uint64(0)
+    _check(L.load().pi_read_down_rows(ws.data_ptr(), ctypes.byref(out), _stream(stream)), "pi_read_down_rows")
     return int(out.value)
 
 

@@ -395,7 +395,11 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
 //    here, in ascending order, with no count needed beforehand, so the slots
 //    and the weights are two round trips, not three.
 // Either way the chunk's rows and h values are staged in LDS so the row loop
-// issues its weight loads with no dependent global load before them.
+// issues its weight loads with no dependent global load before them, and
+// rows whose h is zero for every token are dropped while staging: ReLU
+// zeroes many predicted neurons, and their rows would add nothing.  The
+// workgroups of column slice 0 add the rows they kept to the workspace
+// header's count.
 // ---------------------------------------------------------------------------
 constexpr int kDnThreads = 512;
 constexpr int kDnWaves = kDnThreads / kWave;
@@ -403,24 +407,21 @@ constexpr int kDnUnroll = 8;                 // rows in flight per wave
 constexpr int kDnPiece = kDnThreads;         // list entries staged per round (list form)
 constexpr int kDnSlots = 2 * kDnThreads;     // neurons staged per round (slot form)
 
-// Slot form: the active neurons among [nb0, min(nb0 + kDnSlots, n1)), in
-// ascending order, into rows_l / h_l; returns how many.  Thread t takes
-// neurons nb0 + 2t and nb0 + 2t + 1 (their act and h loads in one round
-// trip); offsets from a wave scan and the wave totals.
-template <int NT, int CAP>
-__device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, const float* __restrict__ h, int d_ff,
-                                           int nb0, int n1, int nt, int* rows_l, float (*h_l)[CAP], int* wsum) {
-  const int lane = lane_id(), wave = wave_id();
-  const int i0 = nb0 + 2 * (int)threadIdx.x, i1 = i0 + 1;
-  const int a0 = i0 < n1 ? act[i0] : -1, a1 = i1 < n1 ? act[i1] : -1;
-  float h0[NT], h1[NT];
+// Whether a staged row adds anything: h nonzero (or NaN) for some token.  A
+// row whose h is exactly zero for every token adds +-0 to sums that start at
+// +0, which changes no bit of them, so it is not read (for finite weights).
+template <int NT>
+__device__ __forceinline__ bool any_nonzero(const float (&hv)[NT], int nt) {
+  bool nz = false;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    h0[j] = j < nt && i0 < n1 ? h[(size_t)j * d_ff + i0] : 0.f;
-    h1[j] = j < nt && i1 < n1 ? h[(size_t)j * d_ff + i1] : 0.f;
-  }
-  const bool v0 = (unsigned)a0 < (unsigned)d_ff, v1 = (unsigned)a1 < (unsigned)d_ff;
-  const int c = (v0 ? 1 : 0) + (v1 ? 1 : 0);
+  for (int j = 0; j < NT; ++j) nz |= j < nt && hv[j] != 0.f;
+  return nz;
+}
+
+// Exclusive offset of this thread's c kept rows among the workgroup's, and
+// the workgroup's total: a wave scan, then the wave totals through LDS.
+__device__ __forceinline__ void kept_offsets(int c, int* wsum, int& pos, int& tot) {
+  const int lane = lane_id(), wave = wave_id();
   int incl = c;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -429,12 +430,34 @@ __device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, cons
   }
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  int pos = incl - c, tot = 0;
+  pos = incl - c;
+  tot = 0;
 #pragma unroll
   for (int w = 0; w < kDnWaves; ++w) {
     pos += w < wave ? wsum[w] : 0;
     tot += wsum[w];
   }
+}
+
+// Slot form: the active neurons among [nb0, min(nb0 + kDnSlots, n1)) with a
+// nonzero h, in ascending order, into rows_l / h_l; returns how many.
+// Thread t takes neurons nb0 + 2t and nb0 + 2t + 1 (their act and h loads in
+// one round trip).
+template <int NT, int CAP>
+__device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, const float* __restrict__ h, int d_ff,
+                                           int nb0, int n1, int nt, int* rows_l, float (*h_l)[CAP], int* wsum) {
+  const int i0 = nb0 + 2 * (int)threadIdx.x, i1 = i0 + 1;
+  const int a0 = i0 < n1 ? act[i0] : -1, a1 = i1 < n1 ? act[i1] : -1;
+  float h0[NT], h1[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    h0[j] = j < nt && i0 < n1 ? h[(size_t)j * d_ff + i0] : 0.f;
+    h1[j] = j < nt && i1 < n1 ? h[(size_t)j * d_ff + i1] : 0.f;
+  }
+  const bool v0 = (unsigned)a0 < (unsigned)d_ff && any_nonzero<NT>(h0, nt);
+  const bool v1 = (unsigned)a1 < (unsigned)d_ff && any_nonzero<NT>(h1, nt);
+  int pos, tot;
+  kept_offsets((v0 ? 1 : 0) + (v1 ? 1 : 0), wsum, pos, tot);
   if (v0) {
     rows_l[pos] = a0;
 #pragma unroll
@@ -445,6 +468,29 @@ __device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, cons
     rows_l[pos] = a1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) h_l[j][pos] = h1[j];
+  }
+  __syncthreads();
+  return tot;
+}
+
+// List form: the entries of list positions [pb, pb + n) (n <= kDnThreads)
+// that name a neuron and have a nonzero h, in list order; returns how many.
+// A malformed entry (outside [0, d_ff)) adds nothing.
+template <int NT, int CAP>
+__device__ __forceinline__ int stage_list(const int32_t* __restrict__ idx, const float* __restrict__ h, int d_ff,
+                                          int pb, int n, int nt, int* rows_l, float (*h_l)[CAP], int* wsum) {
+  const int k = (int)threadIdx.x;
+  const int i = k < n ? idx[pb + k] : -1;
+  float hv[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) hv[j] = j < nt && k < n ? h[(size_t)j * d_ff + pb + k] : 0.f;
+  const bool v = (unsigned)i < (unsigned)d_ff && any_nonzero<NT>(hv, nt);
+  int pos, tot;
+  kept_offsets(v ? 1 : 0, wsum, pos, tot);
+  if (v) {
+    rows_l[pos] = i;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) h_l[j][pos] = hv[j];
   }
   __syncthreads();
   return tot;
@@ -475,7 +521,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
                                                      const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ count_ptr, int max_count,
                                                      const float* __restrict__ h, int nt, int n_chunks,
-                                                     float* __restrict__ part) {
+                                                     float* __restrict__ part,
+                                                     unsigned long long* __restrict__ rows_read) {
   // SLOTS: idx is act[d_ff], h is [nt][d_ff] by neuron, count_ptr unused
   constexpr int E = 16 / sizeof(W);
   constexpr int SW = kWave * E;               // columns per slice
@@ -510,21 +557,15 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
     for (int e = 0; e < E; ++e) acc[j][e] = 0.f;
 
   const char* base = reinterpret_cast<const char*>(w_dt) + (size_t)col * sizeof(W);
+  int n_read = 0;
   for (int pb = k0; pb < k1; pb += CAP) {
     int n;
     if constexpr (SLOTS) {
       n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum);
     } else {
-      n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
-      if ((int)threadIdx.x < n) {
-        const int i = idx[pb + threadIdx.x];
-        rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
-      }
-      __syncthreads();
+      n = stage_list<NT, CAP>(idx, h, d_ff, pb, k1 - pb < kDnPiece ? k1 - pb : kDnPiece, nt, rows_l, h_l, wsum);
     }
+    n_read += n;
     for (int jb = wave; jb < n; jb += kDnWaves * kDnUnroll) {
       u32x4 v[kDnUnroll];
       int rows[kDnUnroll];
@@ -549,6 +590,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
     __syncthreads();
   }
 
+  // The column slices of a chunk read the same rows: slice 0 counts them.
+  if (rows_read && slice == 0 && threadIdx.x == 0 && n_read) atomicAdd(rows_read, (unsigned long long)n_read);
   // Sum the 8 waves in wave order, one token at a time; write the partials.
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -585,7 +628,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
                                                         int d_ff, const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ count_ptr, int max_count,
                                                         const float* __restrict__ h, int nt, int n_chunks,
-                                                        float* __restrict__ part) {
+                                                        float* __restrict__ part,
+                                                        unsigned long long* __restrict__ rows_read) {
   constexpr int CAP = SLOTS ? kDnSlots : kDnPiece;
   __shared__ float red[kDnWaves][kWave * 8];
   __shared__ int rows_l[CAP];
@@ -620,21 +664,15 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
 #pragma unroll
     for (int e = 0; e < kDqCols; ++e) acc[j][e] = 0.f;
 
+  int n_read = 0;
   for (int pb = k0; pb < k1; pb += CAP) {
     int n;
     if constexpr (SLOTS) {
       n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum);
     } else {
-      n = k1 - pb < kDnPiece ? k1 - pb : kDnPiece;
-      if ((int)threadIdx.x < n) {
-        const int i = idx[pb + threadIdx.x];
-        rows_l[threadIdx.x] = (unsigned)i < (unsigned)d_ff ? i : -1;   // a malformed entry adds nothing
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          if (j < nt) h_l[j][threadIdx.x] = h[(size_t)j * d_ff + pb + threadIdx.x];
-      }
-      __syncthreads();
+      n = stage_list<NT, CAP>(idx, h, d_ff, pb, k1 - pb < kDnPiece ? k1 - pb : kDnPiece, nt, rows_l, h_l, wsum);
     }
+    n_read += n;
     for (int jb = wave; jb < n; jb += kDnWaves * kDqUnroll) {
       u32x2 v[kDqUnroll];
       float dsc[kDqUnroll];
@@ -676,6 +714,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
     __syncthreads();
   }
 
+  if (rows_read && slice == 0 && threadIdx.x == 0 && n_read) atomicAdd(rows_read, (unsigned long long)n_read);
   // Sum the 8 waves in wave order, 8 columns per lane per round; write the partials.
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -765,10 +804,11 @@ hipError_t launch_down_form(const SparseArgs& a, int nt, hipStream_t s) {
   const dim3 grid(a.n_slices, a.n_chunks);
   if constexpr (std::is_same<WF, Q4>::value)
     hipLaunchKernelGGL((k_down_q4<NT, SLOTS>), grid, dim3(kDnThreads), 0, s, static_cast<const uint8_t*>(a.w_down_t),
-                       scale_offset<WF>(a), a.d, a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
+                       scale_offset<WF>(a), a.d, a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part,
+                       a.rows_read);
   else
     hipLaunchKernelGGL((k_down<WF, NT, SLOTS>), grid, dim3(kDnThreads), 0, s, static_cast<const WF*>(a.w_down_t), a.d,
-                       a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part);
+                       a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part, a.rows_read);
   return hipGetLastError();
 }
 

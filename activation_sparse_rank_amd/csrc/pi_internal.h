@@ -158,6 +158,8 @@ struct SparseArgs {
   // Per-call fault word of the list's producer; nonzero makes the merge
   // write NaN.  NULL when the list came from no waiting kernel.
   const unsigned* fault = nullptr;
+  // The header's 64-bit count of down-projection rows read; nullable.
+  unsigned long long* rows_read = nullptr;
 };
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
 

@@ -55,25 +55,31 @@ def bytes_compact(cfg, cnt, n_tok=1):
     return n_tok * cfg.d_ff + 4 * cnt + 4
 
 
-def bytes_gather(cfg, cnt, n_tok=1):
-    """Algorithmic bytes of one pi_sparse_ffn call: the active weight rows
-    (each read once for all tokens), their biases and list entries, x and y."""
+def bytes_active(cfg, cnt, down_rows=None):
+    """Bytes of the FFN weight rows a call needs: the up (and gate) rows of
+    the cnt listed neurons, and the down rows that are read -- every listed
+    row, or down_rows when given (the down projection leaves out rows whose
+    h is zero for every token, and counts the rows it reads)."""
+    down = cnt if down_rows is None else down_rows
+    return (cnt * (cfg.n_mat - 1) + down) * _row_bytes(cfg)
+
+
+def bytes_gather(cfg, cnt, n_tok=1, down_rows=None):
+    """Algorithmic bytes of one pi_sparse_ffn call: the weight rows it needs
+    (each read once for all tokens), the biases and list entries of the
+    listed neurons, x and y."""
     xb = 2 if cfg.wtype == "q4_0" else ELEM_BYTES[cfg.wtype]
-    return cnt * cfg.n_mat * _row_bytes(cfg) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model)
+    return bytes_active(cfg, cnt, down_rows) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model)
 
 
-def bytes_active(cfg, cnt):
-    return cnt * cfg.n_mat * _row_bytes(cfg)
-
-
-def bytes_layer(cfg, cnt, n_tok=1):
+def bytes_layer(cfg, cnt, n_tok=1, down_rows=None):
     """Algorithmic bytes of one pi_layer call: both predictor matrices and
-    its bias, x, the active FFN rows (once for all tokens) with their biases,
-    the active list and y."""
+    its bias, x, the FFN rows it needs (once for all tokens), the biases and
+    list entries of the listed neurons, and y."""
     eb = ELEM_BYTES[cfg.pred_wtype]
     xb = 2 if cfg.wtype == "q4_0" else ELEM_BYTES[cfg.wtype]
     return ((cfg.rank * cfg.d_model + cfg.d_ff * cfg.rank) * eb + 4 * cfg.d_ff
-            + bytes_active(cfg, cnt) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model))
+            + bytes_active(cfg, cnt, down_rows) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model))
 
 
 def flops_ffn(cfg, cnt, n_tok):
@@ -121,6 +127,7 @@ def load_traffic(workload):
 
 
 def _time_graph(graph, reps, stream):
+    """ms per replay of graph over reps replays, after one untimed replay."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     graph.replay()
@@ -369,6 +376,7 @@ def main(argv=None):
             step(t)
     torch.cuda.synchronize()
     # the timed steps, repeated: each repeat replays the same K steps
+    rows_before = pi.read_down_rows(ws, stream)
     rep_ms = []
     for r in range(max(1, args.repeats)):
         start = torch.cuda.Event(enable_timing=True)
@@ -387,6 +395,8 @@ def main(argv=None):
     ms_step = ms_total / args.steps
     layer_tok_s = args.steps * L * B / (ms_total / 1e3)
     flags_step = pi.read_flags(ws, stream)
+    # down-projection rows the timed layer calls read (the workspace header's count)
+    down_mean = (pi.read_down_rows(ws, stream) - rows_before) / (len(rep_ms) * args.steps * L)
     if flags_step:
         print(f"[bench] fault flags raised during the timed steps: {flags_step:#x}", file=sys.stderr, flush=True)
 
@@ -412,7 +422,7 @@ def main(argv=None):
 
     # ---------------- per-call timing: predict, compact, sparse FFN ----------------
     # inputs of the last timed step; idx/count of every layer from g_pc
-    ws_s = torch.empty(pi.workspace_bytes(None, ffns[0], B), dtype=torch.uint8, device=dev)
+    ws_s = torch.zeros(pi.workspace_bytes(None, ffns[0], B), dtype=torch.uint8, device=dev)   # header clear
     g_pred, g_comp, g_sp = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_pred, stream=stream):
         for li in range(L):
@@ -433,16 +443,20 @@ def main(argv=None):
             for k in mat_keys:
                 for view, rb in matrix_rows(cfg, layers[li], k):
                     pi.gather_read(view, idx[li], cnt[li:li + 1], row_bytes=rb, max_count=f, out=gr_out)
+    sp_rows0 = pi.read_down_rows(ws_s, stream)
     with torch.cuda.stream(stream):
         ms_pred = _time_graph(g_pred, args.reps, stream) / L
         ms_comp = _time_graph(g_comp, args.reps, stream) / L
         ms_sp = _time_graph(g_sp, args.reps, stream) / L
         ms_gr = _time_graph(g_gr, args.reps, stream) / L
+    sp_down = (pi.read_down_rows(ws_s, stream) - sp_rows0) / ((args.reps + 1) * L)
     last_cnt = cnt.cpu().numpy().astype(np.int64)
+    last_mean = float(last_cnt.mean())
     b_pred = bytes_predict(cfg, B)
     b_comp = float(np.mean([bytes_compact(cfg, c, B) for c in last_cnt]))
-    b_sp = float(np.mean([bytes_gather(cfg, c, B) for c in last_cnt]))
-    b_act = float(np.mean([bytes_active(cfg, c) for c in last_cnt]))
+    b_sp = bytes_gather(cfg, last_mean, B, sp_down)
+    b_act = bytes_active(cfg, last_mean, sp_down)
+    b_listed = bytes_active(cfg, last_mean)          # every listed row of every matrix
 
     traffic_table = load_traffic(f"{cfg.name} decode batch {B}")
 
@@ -463,8 +477,9 @@ def main(argv=None):
     # of an 8 GiB buffer, the reference the path's streams are compared with
     stream_gbps = measure_stream(pi, dev, stream)
 
-    # whole-layer bytes per layer call, averaged over the timed steps
-    b_layer = float(np.mean([bytes_layer(cfg, c, B) for c in counts.flat]))
+    # whole-layer bytes per layer call, averaged over the timed steps (bytes
+    # are linear in the list length and the down rows read)
+    b_layer = bytes_layer(cfg, cnt_mean, B, down_mean)
     ms_layer = ms_step / L
     kern = _kernels(cfg, B)
     layer_roof = roof(f"pi_layer ({kern})", b_layer, ms_layer)
@@ -474,7 +489,7 @@ def main(argv=None):
                     "bytes_per_launch": int(b_comp)},
         "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, B)})", b_sp, ms_sp),
     }
-    gather_read_gbps = round(b_act / (ms_gr * 1e-3) / 1e9, 1)
+    gather_read_gbps = round(b_listed / (ms_gr * 1e-3) / 1e9, 1)
     for r in (layer_roof, parts["predict"], parts["gather"]):
         r["stream_read_gbps"] = stream_gbps
         r["frac_of_stream_read"] = round(r["achieved"] / stream_gbps, 4)
@@ -482,8 +497,8 @@ def main(argv=None):
     parts["gather"]["active_weight_gbps"] = round(b_act / (ms_sp * 1e-3) / 1e9, 1)
     parts["gather"]["active_weight_frac"] = round(b_act / (ms_sp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
     parts["gather"]["frac_of_gather_read"] = round(parts["gather"]["active_weight_gbps"] / gather_read_gbps, 4)
-    parts["gather_read"] = {"what": "pi_gather_read of the same active rows of every weight matrix, no arithmetic",
-                            "avg_us_per_layer": round(ms_gr * 1e3, 3), "bytes_per_layer": int(b_act),
+    parts["gather_read"] = {"what": "pi_gather_read of every listed row of every weight matrix, no arithmetic",
+                            "avg_us_per_layer": round(ms_gr * 1e3, 3), "bytes_per_layer": int(b_listed),
                             "gbps": gather_read_gbps}
 
     out = {
@@ -515,6 +530,7 @@ def main(argv=None):
         "roofline": layer_roof,
         "roofline_parts": parts,
         "count_mean": round(cnt_mean, 1),
+        "down_rows_mean": round(down_mean, 1),
         "count_min": int(counts.min()),
         "count_max": int(counts.max()),
         "gen_seconds": round(t_gen, 1),
@@ -527,7 +543,7 @@ def main(argv=None):
         for li in range(L):
             x_pr[li] = workload.make_tokens(cfg, li, n, dev, args.seed, stream=1)
         y_pr = torch.empty((L, n, d), dtype=torch.float32, device=dev)
-        ws_m = torch.empty(pi.workspace_bytes(preds[0], ffns[0], n), dtype=torch.uint8, device=dev)
+        ws_m = torch.zeros(pi.workspace_bytes(preds[0], ffns[0], n), dtype=torch.uint8, device=dev)
         mask_m = torch.empty((L, n, f), dtype=torch.uint8, device=dev)
         idx_m = torch.empty((L, f), dtype=torch.int32, device=dev)
         cnt_m = torch.zeros((L,), dtype=torch.int32, device=dev)
@@ -550,10 +566,12 @@ def main(argv=None):
             for li in range(L):
                 pi.sparse_ffn(ffns[li], x_pr[li], idx_m[li], cnt_m[li:li + 1], y_pr[li], ws=ws_ms)
         reps = max(2, args.reps // 4)
+        ml_rows0 = pi.read_down_rows(ws_m, stream)
         with torch.cuda.stream(stream):
             ms_ml = _time_graph(g_ml, reps, stream) / L
             ms_mp = _time_graph(g_mp, reps, stream) / L
             ms_ms = _time_graph(g_ms, reps, stream) / L
+        ml_down = (pi.read_down_rows(ws_m, stream) - ml_rows0) / ((reps + 1) * L)
         # the union's rows of every weight matrix read with no arithmetic
         g_mgr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_mgr, stream=stream):
@@ -564,15 +582,17 @@ def main(argv=None):
         with torch.cuda.stream(stream):
             ms_mgr = _time_graph(g_mgr, reps, stream) / L
         uc = cnt_m.cpu().numpy().astype(np.int64)
-        b_ml = float(np.mean([bytes_layer(cfg, c, n) for c in uc]))
-        b_ms = float(np.mean([bytes_gather(cfg, c, n) for c in uc]))
+        uc_mean = float(uc.mean())
+        b_ml = bytes_layer(cfg, uc_mean, n, ml_down)
+        b_ms = bytes_gather(cfg, uc_mean, n)
         fl = float(np.mean([flops_ffn(cfg, c, n) for c in uc]))
         tflops = fl / (ms_ms * 1e-3) / 1e12
         mk = _kernels(cfg, n)
         out["multi_token"] = {
             "what": f"one prompt of {n} tokens per layer, per-token masks OR-ed into one list",
             "n_tok": n,
-            "union_count_mean": round(float(uc.mean()), 1),
+            "union_count_mean": round(uc_mean, 1),
+            "down_rows_mean": round(ml_down, 1),
             "layer_tokens_per_s": round(n / (ms_ml * 1e-3), 1),
             "layer": roof(f"pi_layer ({mk})", b_ml, ms_ml),
             "predict": roof(f"pi_predict ({_pred_kernels(cfg, n)})", bytes_predict(cfg, n), ms_mp),

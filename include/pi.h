@@ -124,6 +124,15 @@ size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n
  *     in-kernel list that leaves its count unpublished, so the waits of the
  *     workgroups after it give up (0 = none).
  * Both hooks exist to force the give-up path from the host; leave them 0.
+ *   words PI_WS_DOWN_ROWS, PI_WS_DOWN_ROWS + 1: a 64-bit count (low word
+ *     first) of the w_down_t rows that the down projections of calls on this
+ *     workspace have read, summed over calls; read it with pi_read_down_rows.
+ *     The list-path down projection (one or two tokens; Q4_0's tile of two)
+ *     reads only the listed rows whose h is nonzero for at least one token:
+ *     a row whose h is exactly zero for every token adds nothing to y, so
+ *     leaving it out changes no result (for finite weights).  The
+ *     matrix-core down projection reads, and counts, every listed row once
+ *     per token tile.
  *
  * With one or two tokens pi_layer needs no list: the kernel that decides a
  * neuron writes a per-neuron slot (its index, or -1), and the down
@@ -140,21 +149,28 @@ size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n
 #define PI_WS_FLAGS 0
 #define PI_WS_WAIT_POLLS 1
 #define PI_WS_SKIP_PUBLISH 2
+#define PI_WS_DOWN_ROWS 4
 #define PI_FLAG_WAIT_EXPIRED 1u /* an in-kernel wait gave up; that call's y is all NaN            */
 #define PI_FLAG_FP16_RANGE 2u   /* a value the matrix-core path keeps in fp16 (the FFN's H, or the
                                    predictor's t) was not finite after rounding to fp16; the
                                    affected outputs are inf or NaN                              */
 
-/* Zero the header of ws (flags and test hooks).  Asynchronous on stream, a
+/* Zero the header of ws (flags, test hooks, row count).  Asynchronous on stream, a
  * kernel (no memset), so it may be captured into a graph.
  * Errors: NULL ws, ws not 16-byte aligned.  */
 pi_status pi_clear_flags(void* ws, void* stream);
 
-/* Read the flags word of ws into *flags (host memory).  The one SYNCHRONOUS
- * call of this library: it waits for the work queued on stream before it
- * returns, so the flags of every earlier call on that stream are included.
+/* Read the flags word of ws into *flags (host memory).  One of the two
+ * SYNCHRONOUS calls of this library (with pi_read_down_rows): it waits for
+ * the work queued on stream before it returns, so the flags of every earlier
+ * call on that stream are included.
  * Errors: NULL pointers, ws not 16-byte aligned, PI_E_HIP.  */
 pi_status pi_read_flags(const void* ws, uint32_t* flags, void* stream);
+
+/* Read the header's count of down-projection rows read (PI_WS_DOWN_ROWS)
+ * into *rows (host memory).  SYNCHRONOUS, like pi_read_flags.
+ * Errors: NULL pointers, ws not 16-byte aligned, PI_E_HIP.  */
+pi_status pi_read_down_rows(const void* ws, uint64_t* rows, void* stream);
 
 /* Predict which neurons each token activates.
  *   x:      [n_tok][d_model], dtype xtype == pred->wtype

@@ -187,6 +187,10 @@ def test_flag_calls_reject(lib):
     assert lib.pi_read_flags(None, ctypes.byref(out), None) == L.PI_E_NULL
     assert lib.pi_read_flags(FAKE, None, None) == L.PI_E_NULL
     assert lib.pi_read_flags(FAKE_ODD, ctypes.byref(out), None) == L.PI_E_ALIGN
+    rows = ctypes.c_uint64(0)
+    assert lib.pi_read_down_rows(None, ctypes.byref(rows), None) == L.PI_E_NULL
+    assert lib.pi_read_down_rows(FAKE, None, None) == L.PI_E_NULL
+    assert lib.pi_read_down_rows(FAKE_ODD, ctypes.byref(rows), None) == L.PI_E_ALIGN
 
 
 def test_workspace_has_header(lib):

@@ -36,3 +36,16 @@ def test_gather_and_predict_bytes():
     cfg = workload.get_config("falcon40b")
     assert bench.bytes_gather(cfg, 100) == 100 * 2 * 16384 + 800 + 8192 * 2 + 8192 * 4
     assert bench.bytes_predict(cfg) == (1024 * 8192 + 32768 * 1024) * 2 + 4 * 32768 + 8192 * 2 + 32768
+
+
+def test_down_rows_read_replace_listed_down_rows():
+    # The down projection leaves out rows whose h is zero for every token and
+    # counts the rows it reads; the bytes then take that count for the down
+    # matrix only (the up and gate rows of every listed neuron are still read).
+    cfg = workload.get_config("falcon40b")
+    rb = 8192 * 2
+    assert bench.bytes_active(cfg, 3277, 1456) == (3277 + 1456) * rb
+    assert bench.bytes_layer(cfg, 3277, 1, 1456) == bench.bytes_layer(cfg, 3277) - (3277 - 1456) * rb
+    assert bench.bytes_gather(cfg, 3277, 1, 3277) == bench.bytes_gather(cfg, 3277)
+    ll = workload.get_config("llama70b")
+    assert bench.bytes_active(ll, 2867, 1000) == (2 * 2867 + 1000) * rb
