@@ -280,6 +280,34 @@ struct TokStep {
   }
 };
 
+// The same operands read from the row-major token tile x[t][d] (each lane
+// the 16 bytes of its token), with a copy into the step-major layout above
+// (store_step), so that a kernel which reads every step of x once can leave
+// the copy for the kernels that read it many times.
+template <int NB>
+struct TokStepRM {
+  u32x4 v[NB][4];
+  __device__ __forceinline__ void load(const f16* x, int d, int nt, int st, int g, int n16) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int t = nb * 16 + n16;
+      ld_k128(x + (size_t)(t < nt ? t : 0) * d + (size_t)st * kMuK, t < nt, g, false, v[nb]);
+    }
+  }
+  // xs[st][t][32s + 8g .. +8] = the lane's operand of sub-step s (natural order)
+  __device__ __forceinline__ void store_step(f16* xs, int nt, int st, int g, int n16) const {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int t = nb * 16 + n16;
+      if (t < nt) {
+        f16* dst = xs + ((size_t)st * nt + t) * kMuK + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(dst + 32 * s) = v[nb][s];
+      }
+    }
+  }
+};
+
 // Run steps [s0, s1) with two register stages: the loads of step st+1 are
 // issued before step st is multiplied.  load(stage, st) and mul(stage) are
 // the caller's.
@@ -875,7 +903,8 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
 // products and a threshold).  Same tiling as k_mup, over all rows:
 //   k_mp1    -- part[s][j][r] = sum over k in split s of p1[r][k] * x[j][k]
 //               (the k range is split over the grid's y dimension, then over
-//               the 4 waves);
+//               the 4 waves), x read row-major; it also leaves the step-major
+//               copy of x for the fp16 FFN;
 //   k_tsplit -- t = the splits added in order (fp32), and t_hi = fp16(t),
 //               t_lo = fp16(t - t_hi);
 //   k_mp2    -- l[j][i] = p2[i] . t[j] + c[i]; mask = l > theta (per token,
@@ -885,8 +914,10 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
 // ---------------------------------------------------------------------------
 template <int NB>
 __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, const f16* __restrict__ x, int d,
-                                                    int rank, int nt, float* __restrict__ part) {
-  // x: the step-major copy of the token tile (k_xstep)
+                                                    int rank, int nt, float* __restrict__ part,
+                                                    f16* __restrict__ xs) {
+  // x: the row-major token tile; the workgroups of row block 0 also write
+  // the step-major copy xs (nullable) of the steps they read
   constexpr int NQ = kMuMB * NB;
   __shared__ float red[kMuWaves][NQ][4][kWave];
   const int lane = lane_id(), wave = wave_id();
@@ -908,13 +939,16 @@ __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, 
   const int s0 = c0 + wave * (c1 - c0) / kMuWaves, s1 = c0 + (wave + 1) * (c1 - c0) / kMuWaves;
 #pragma unroll
   for (int mb = 0; mb < kMuMB; ++mb) row[mb] = rv[mb] ? row[mb] : 0;
+  const bool copy = xs != nullptr && blockIdx.x == 0;
   struct Step {
     RowStep<f16, kMuMB> w;
-    TokStep<NB> x;
+    TokStepRM<NB> x;
+    int st;
   };
   auto load = [&](Step& S, int st) {
     S.w.load(p1, 0, row, rv, d, st * kMuK, g);
-    S.x.load(x, nt, st, g, n16);
+    S.x.load(x, d, nt, st, g, n16);
+    S.st = st;
   };
   auto mul = [&](const Step& S) {
 #pragma unroll
@@ -923,6 +957,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, 
       for (int mb = 0; mb < kMuMB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.x.v[nb][s], acc[mb * NB + nb]);
+    if (copy) S.x.store_step(xs, nt, S.st, g, n16);
   };
   Step S0, S1;
   pipeline2(s0, s1, S0, S1, load, mul);
@@ -1514,13 +1549,9 @@ hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x,
   f16* th = reinterpret_cast<f16*>(ws + up256((size_t)splits * kMfmaTile * rank * sizeof(float)));
   f16* tl = th + (size_t)kMfmaTile * rank;
   f16* xs = tl + (size_t)kMfmaTile * rank;
-  const int n_groups = nt * d / 8;
-  hipLaunchKernelGGL((k_xstep<false>), dim3((n_groups + 255) / 256), dim3(256), 0, s, x, nt, d, xs);
+  hipLaunchKernelGGL((k_mp1<NB>), dim3((rank + kMuRows - 1) / kMuRows, splits), dim3(kMuThreads), 0, s, p1, x, d,
+                     rank, nt, part, xs);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_mp1<NB>), dim3((rank + kMuRows - 1) / kMuRows, splits), dim3(kMuThreads), 0, s, p1, xs, d,
-                     rank, nt, part);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (xs_out) *xs_out = xs;
   const int grid2 = NB >= 3 ? (d_ff + kMpRows - 1) / kMpRows : (d_ff + kMuRows - 1) / kMuRows;
