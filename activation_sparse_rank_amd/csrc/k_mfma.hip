@@ -248,6 +248,33 @@ struct RowStepT {
   }
 };
 
+// RowStepT with every lane loading (rows past the count read a valid stand-in
+// row) and the stand-in rows zeroed when the operands are formed, so the
+// loads carry no lane condition and the compiler can count the ones in
+// flight exactly (a load under a lane condition, or a load whose issue
+// depends on a branch, makes it wait for every load issued so far).
+template <int MB>
+struct RowStepTU {
+  u32x4 v[MB][4];
+  __device__ __forceinline__ void load(const f16* w, const int (&rowt)[MB][4], int d, int kb, int lane) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[mb][i] = ld_nt(reinterpret_cast<const char*>(w + (size_t)rowt[mb][i] * d + kb) + 16 * (lane & 15));
+  }
+  __device__ __forceinline__ void operands(int mb, const bool (&rvt)[MB][4], u32x4* buf, int lane,
+                                           u32x4 (&a)[4]) const {
+    const int q = lane >> 4, u = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[(4 * i + q) * kTStride + u] = rvt[mb][i] ? v[mb][i] : u32x4{0, 0, 0, 0};
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // the writes land before any lane reads
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = buf[u * kTStride + 4 * s + q];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // and the reads before the next block's writes
+  }
+};
+
 // Row indices of the transposed load: position 4i + l/16 of each block, from
 // the lane that holds it in the operand layout (position l%16).
 template <int MB>
@@ -290,8 +317,8 @@ struct TokStepRM {
   __device__ __forceinline__ void load(const f16* x, int d, int nt, int st, int g, int n16) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int t = nb * 16 + n16;
-      ld_k128(x + (size_t)(t < nt ? t : 0) * d + (size_t)st * kMuK, t < nt, g, false, v[nb]);
+      const int t = nb * 16 + n16;                 // slots past nt read the last token (never stored)
+      ld_k128(x + (size_t)(t < nt ? t : nt - 1) * d + (size_t)st * kMuK, true, g, false, v[nb]);
     }
   }
   // xs[st][t][32s + 8g .. +8] = the lane's operand of sub-step s (natural order)
@@ -311,15 +338,27 @@ struct TokStepRM {
 // Run steps [s0, s1) with two register stages: the loads of step st+1 are
 // issued before step st is multiplied.  load(stage, st) and mul(stage) are
 // the caller's.
+// The steady state issues every load unconditionally and the last one or two
+// steps are peeled, so no load's issue depends on a branch: with loads that
+// also carry no lane condition the compiler can then wait for exactly the
+// step it multiplies (a conditional issue makes it wait for every load).
 template <typename Stage, typename Load, typename Mul>
 __device__ __forceinline__ void pipeline2(int s0, int s1, Stage& A, Stage& B, Load load, Mul mul) {
   if (s0 >= s1) return;
   load(A, s0);
-  for (int st = s0; st < s1; st += 2) {
-    if (st + 1 < s1) load(B, st + 1);
+  int st = s0;
+  for (; st + 2 < s1; st += 2) {
+    load(B, st + 1);
     mul(A);
-    if (st + 2 < s1) load(A, st + 2);
-    if (st + 1 < s1) mul(B);
+    load(A, st + 2);
+    mul(B);
+  }
+  if (st + 1 < s1) {
+    load(B, st + 1);
+    mul(A);
+    mul(B);
+  } else {
+    mul(A);
   }
 }
 
@@ -408,16 +447,18 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   bool rvt[MB][4];
   if constexpr (TR) rows_for_load<MB>(row, rv, lane, rowt, rvt);
   u32x4* wbuf = &w_l[TR ? wave : 0][0];
-  using Rows = typename std::conditional<TR, RowStepT<MB>, RowStep<WF, MB>>::type;
+  // fp16 rows: every lane loads (stand-in rows and token slots; see RowStepTU)
+  using Rows = typename std::conditional<TR, RowStepTU<MB>, RowStep<WF, MB>>::type;
+  using Toks = typename std::conditional<TR, TokStepClamped<NB>, TokStep<NB>>::type;
   struct Step {
     Rows up;
     RowStep<WF, GATED ? MB : 1> gate;
-    TokStep<NB> x;
+    Toks x;
   };
   auto load = [&](Step& S, int st) {
     const int kb = st * kMuK;
     if constexpr (TR)
-      S.up.load(static_cast<const f16*>(w_up), rowt, rvt, d, kb, lane);
+      S.up.load(static_cast<const f16*>(w_up), rowt, d, kb, lane);
     else
       S.up.load(w_up, scale_off, row, rv, d, kb, g);
     if constexpr (GATED) S.gate.load(w_gate, scale_off, row, rv, d, kb, g);
@@ -428,7 +469,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
     for (int mb = 0; mb < MB; ++mb) {
       u32x4 a[4], ga[4];
       if constexpr (TR)
-        S.up.operands(mb, wbuf, lane, a);
+        S.up.operands(mb, rvt, wbuf, lane, a);
       else
         S.up.operands(mb, a);
       if constexpr (GATED) S.gate.operands(mb, ga);
@@ -628,7 +669,83 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
       if constexpr (GATED) S.gate.load(w_gate, scale_off, row, rv, d, st * kMuK, g);
     }
   };
+  const bool whole = s1 > s0 && (s1 - s0) % kMxPiece == 0;
+  if constexpr (F16) {
+    if (whole) {
+      // Whole pieces: a branch-free software pipeline.  Each step's rows are
+      // requested one step ahead, and the next piece's x units together with
+      // its first step's rows during the piece's last step, every load
+      // unconditional, so each wait covers exactly the loads it needs.
+      constexpr int XU = kMxPiece * LU / kMxThreads;   // x units per thread per piece
+      const int su = nt * (kMuK / 8);
+      u32x4 xr[XU];
+      auto x_load = [&](int p0) {
+#pragma unroll
+        for (int k = 0; k < XU; ++k) {
+          const int e = threadIdx.x + kMxThreads * k;
+          const int q = e / LU, r = e - q * LU;
+          const int rr = r < su ? r : su - 1;          // slots past nt: a valid stand-in, zeroed on store
+          xr[k] = ld16(xs + ((size_t)(p0 + q) * nt) * kMuK + (size_t)rr * 8);
+        }
+      };
+      auto x_store = [&]() {
+#pragma unroll
+        for (int k = 0; k < XU; ++k) {
+          const int e = threadIdx.x + kMxThreads * k;
+          const int q = e / LU, r = e - q * LU;
+          x_l[q][(r >> 4) * kTokStride + (r & 15)] = r < su ? xr[k] : u32x4{0, 0, 0, 0};
+        }
+      };
+      RowStepTU<kMxMB> S0, S1;
+      auto rows = [&](RowStepTU<kMxMB>& S, int st) { S.load(static_cast<const f16*>(w_up), rowt, d, st * kMuK, lane); };
+      auto step = [&](const RowStepTU<kMxMB>& S, int q) {
+        u32x4 a[kMxMB][4];
+#pragma unroll
+        for (int mb = 0; mb < kMxMB; ++mb) S.operands(mb, rvt, wbuf, lane, a[mb]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          u32x4 b[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) b[nb] = x_l[q][(nb * 16 + n16) * kTokStride + 4 * s + g];
+#pragma unroll
+          for (int mb = 0; mb < kMxMB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) au[mb][nb] = mfma(a[mb][s], b[nb], au[mb][nb]);
+        }
+      };
+      // piece p0 (its x in x_l, the rows of its first step in S0)
+      auto piece = [&](int p0, auto has_next) {
+        static_assert(kMxPiece == 4, "the unrolled piece is 4 steps");
+        rows(S1, p0 + 1);
+        step(S0, 0);
+        rows(S0, p0 + 2);
+        step(S1, 1);
+        rows(S1, p0 + 3);
+        step(S0, 2);
+        if constexpr (decltype(has_next)::value) {
+          x_load(p0 + kMxPiece);
+          rows(S0, p0 + kMxPiece);
+        }
+        step(S1, 3);
+        if constexpr (decltype(has_next)::value) {
+          __syncthreads();                             // every wave is done with this piece's x
+          x_store();
+          __syncthreads();
+        }
+      };
+      x_load(s0);
+      rows(S0, s0);
+      x_store();
+      __syncthreads();
+      int p0 = s0;
+      for (; p0 + kMxPiece < s1; p0 += kMxPiece) piece(p0, std::true_type{});
+      piece(p0, std::false_type{});
+    }
+  }
   for (int p0 = s0; p0 < s1; p0 += kMxPiece) {
+    if constexpr (F16) {
+      if (whole) break;                                // done above
+    }
     const int np = s1 - p0 < kMxPiece ? s1 - p0 : kMxPiece;
     Step cur;
     load(cur, p0);                                  // the first step's rows go out before the staging
@@ -940,13 +1057,17 @@ __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, 
 #pragma unroll
   for (int mb = 0; mb < kMuMB; ++mb) row[mb] = rv[mb] ? row[mb] : 0;
   const bool copy = xs != nullptr && blockIdx.x == 0;
+  // every lane loads (rows past rank read row 0; their sums are never stored)
+  bool all[kMuMB];
+#pragma unroll
+  for (int mb = 0; mb < kMuMB; ++mb) all[mb] = true;
   struct Step {
     RowStep<f16, kMuMB> w;
     TokStepRM<NB> x;
     int st;
   };
   auto load = [&](Step& S, int st) {
-    S.w.load(p1, 0, row, rv, d, st * kMuK, g);
+    S.w.load(p1, 0, row, all, d, st * kMuK, g);
     S.x.load(x, d, nt, st, g, n16);
     S.st = st;
   };
@@ -1106,6 +1227,8 @@ __global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, 
   const int s0 = wave * ns / kMuWaves, s1 = (wave + 1) * ns / kMuWaves;
 #pragma unroll
   for (int mb = 0; mb < kMuMB; ++mb) row[mb] = rv[mb] ? row[mb] : 0;
+  // (every lane loading, as in k_mp1, made this kernel 0.7 us slower per
+  // Falcon layer at 8 tokens: its loads stay conditional)
   struct Step {
     RowStep<f16, kMuMB> w;
     TokStep<NB> hi, lo;
