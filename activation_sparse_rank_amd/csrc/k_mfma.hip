@@ -1440,7 +1440,82 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ns = rank / kMuK;
   const int su = nt * (kMuK / 8);                 // units of one step of the nt real tokens
-  for (int p0 = 0; p0 < ns; p0 += kMpPiece) {
+  const bool whole = ns % kMpPiece == 0;
+  if (whole) {
+    // Whole pieces: the unrolled branch-free pipeline of k_mup_wide.  Every
+    // lane loads (rows past d_ff read row 0 and are never stored; token
+    // slots past nt read a valid unit and are zeroed in LDS), and the next
+    // piece's t units and first rows go out during the piece's last step.
+    constexpr int XU = kMpPiece * LU / kMpThreads;   // units of t_hi (and of t_lo) per thread per piece
+    u32x4 hr[XU], lr[XU];
+    auto t_load = [&](int p0) {
+#pragma unroll
+      for (int k = 0; k < XU; ++k) {
+        const int e = threadIdx.x + kMpThreads * k;
+        const int q = e / LU, r = e - q * LU;
+        const size_t o = (size_t)(p0 + q) * nt * kMuK + (size_t)(r < su ? r : su - 1) * 8;
+        hr[k] = ld16(th + o);
+        lr[k] = ld16(tl + o);
+      }
+    };
+    auto t_store = [&]() {
+#pragma unroll
+      for (int k = 0; k < XU; ++k) {
+        const int e = threadIdx.x + kMpThreads * k;
+        const int q = e / LU, r = e - q * LU;
+        const int u = (r >> 4) * kTokStride + (r & 15);
+        th_l[q][u] = r < su ? hr[k] : u32x4{0, 0, 0, 0};
+        tl_l[q][u] = r < su ? lr[k] : u32x4{0, 0, 0, 0};
+      }
+    };
+    bool all[1] = {true};
+    RowStep<f16, 1> S0, S1;
+    auto rows = [&](RowStep<f16, 1>& S, int st) { S.load(p2, 0, row, all, rank, st * kMuK, g); };
+    auto step = [&](const RowStep<f16, 1>& S, int q) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 bh[NB], bl[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int u = (nb * 16 + n16) * kTokStride + 4 * s + g;
+          bh[nb] = th_l[q][u];
+          bl[nb] = tl_l[q][u];
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[nb] = mfma(S.v[0][s], bh[nb], acc[nb]);
+          acc[nb] = mfma(S.v[0][s], bl[nb], acc[nb]);
+        }
+      }
+    };
+    auto piece = [&](int p0, auto has_next) {
+      static_assert(kMpPiece == 4, "the unrolled piece is 4 steps");
+      rows(S1, p0 + 1);
+      step(S0, 0);
+      rows(S0, p0 + 2);
+      step(S1, 1);
+      rows(S1, p0 + 3);
+      step(S0, 2);
+      if constexpr (decltype(has_next)::value) {
+        t_load(p0 + kMpPiece);
+        rows(S0, p0 + kMpPiece);
+      }
+      step(S1, 3);
+      if constexpr (decltype(has_next)::value) {
+        __syncthreads();                               // every wave is done with this piece's t
+        t_store();
+        __syncthreads();
+      }
+    };
+    t_load(0);
+    rows(S0, 0);
+    t_store();
+    __syncthreads();
+    int p0 = 0;
+    for (; p0 + kMpPiece < ns; p0 += kMpPiece) piece(p0, std::true_type{});
+    piece(p0, std::false_type{});
+  }
+  for (int p0 = 0; p0 < ns && !whole; p0 += kMpPiece) {
     const int np = ns - p0 < kMpPiece ? ns - p0 : kMpPiece;
     RowStep<f16, 1> cur;
     cur.load(p2, 0, row, rv, rank, p0 * kMuK, g);  // the first step's rows go out before the staging
