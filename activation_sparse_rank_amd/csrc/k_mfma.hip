@@ -210,6 +210,17 @@ struct RowStep<Q4, MB> {
 #pragma unroll
     for (int s = 0; s < 4; ++s) a[s] = q4_dequant8(dw(code[mb], s), s2);
   }
+  // the code groups only (every lane loads; the scales come from elsewhere)
+  __device__ __forceinline__ void load_codes(const void* w, const int (&row)[MB], int d, int kb, int g) {
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) code[mb] = ld_nt(wb + ((size_t)row[mb] * (d / 32) + kb / 32 + g) * 16);
+  }
+  __device__ __forceinline__ void operands(int mb, f16 scale, u32x4 (&a)[4]) const {
+    const f16x2 s2{scale, scale};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = q4_dequant8(dw(code[mb], s), s2);
+  }
 };
 
 // The same step of MB 16-row blocks of fp16 rows, loaded the way a gather
@@ -415,6 +426,8 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   constexpr bool TR = std::is_same<WF, f16>::value && !GATED;   // transposed row loads (RowStepT)
   __shared__ float red[kMuWaves][NQ][4][kWave];
   __shared__ u32x4 w_l[TR ? kMuWaves : 1][TR ? 16 * kTStride : 1];
+  constexpr bool Q = std::is_same<WF, Q4>::value;
+  __shared__ u32x4 sc_l[Q ? kMuWaves : 1][Q ? MB : 1][16][Q ? 4 : 1];   // Q4_0: a chunk's scales per row
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -494,14 +507,47 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
     bool all[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) all[mb] = true;
+    // The up rows' scales of a whole chunk (4 per step, 8 bytes per step and
+    // row, contiguous) in one 16-byte load per lane -- lane (g, n16) takes
+    // unit g % SU of row n16 -- staged in this wave's LDS: a 2-byte load per
+    // lane and step otherwise costs as many memory instructions as the codes.
+    // Needs 16-byte aligned scale rows (d % 256 == 0) and whole chunks.
+    constexpr int SU = kQPre / 2;                   // 16-byte scale units per row per chunk
+    const int nbk = d / 32;
+    const bool sc_chunk = !GATED && nbk % 8 == 0 && (s1 - s0) % kQPre == 0;
+    const uint8_t* sc_base = static_cast<const uint8_t*>(w_up) + scale_off;
     for (int c0 = s0; c0 < s1; c0 += kQPre) {
       RowStep<WF, MB> up[kQPre];
       RowStep<WF, GATED ? MB : 1> gt[GATED ? kQPre : 1];
+      bool chunked = false;
+      if constexpr (!GATED) {
+        if (sc_chunk) {
+          u32x4 su[MB];
 #pragma unroll
-      for (int j = 0; j < kQPre; ++j) {
-        const int st = c0 + j < s1 ? c0 + j : s1 - 1;
-        up[j].load(w_up, scale_off, row, all, d, st * kMuK, g);
-        if constexpr (GATED) gt[j].load(w_gate, scale_off, row, all, d, st * kMuK, g);
+          for (int mb = 0; mb < MB; ++mb)
+            su[mb] = ld_nt(sc_base + ((size_t)row[mb] * nbk + (size_t)c0 * 4) * 2 + 16 * (g % SU));
+#pragma unroll
+          for (int j = 0; j < kQPre; ++j) up[j].load_codes(w_up, row, d, (c0 + j) * kMuK, g);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            if (g < SU) sc_l[wave][mb][n16][g] = su[mb];
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // the scales land before any lane reads
+#pragma unroll
+          for (int j = 0; j < kQPre; ++j)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              up[j].sc[mb] = reinterpret_cast<const f16*>(&sc_l[wave][mb][n16][0])[4 * j + g];
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // and are read before the next chunk's writes
+          chunked = true;
+        }
+      }
+      if (!chunked) {
+#pragma unroll
+        for (int j = 0; j < kQPre; ++j) {
+          const int st = c0 + j < s1 ? c0 + j : s1 - 1;
+          up[j].load(w_up, scale_off, row, all, d, st * kMuK, g);
+          if constexpr (GATED) gt[j].load(w_gate, scale_off, row, all, d, st * kMuK, g);
+        }
       }
       TokStepClamped<NB> xt[2];
       xt[0].load(x, nt, c0, g, n16);
