@@ -252,7 +252,7 @@ def matrix_rows(cfg, lw, key):
 def _pred_kernels(cfg, n_tok):
     """Kernels of one pi_predict call (labels only)."""
     if cfg.pred_wtype == "f16" and cfg.d_model % 128 == 0 and cfg.rank % 128 == 0 and n_tok > 2:
-        return f"k_xstep + k_mp1 + k_tsplit + {'k_mp2_wide' if min(n_tok, 64) > 32 else 'k_mp2'}"
+        return f"k_mp1 + k_tsplit + {'k_mp2_wide' if min(n_tok, 64) > 32 else 'k_mp2'}"
     return "k_pred1 + k_pred2"
 
 
@@ -272,9 +272,10 @@ def _kernels(cfg, n_tok):
     if n_tok <= _tile(cfg) and pred == "k_pred1 + k_pred2" and _ffn_kernels(cfg, n_tok).startswith("k_up"):
         return f"k_pred1 + k_pred_up + {'k_down_q4' if cfg.wtype == 'q4_0' else 'k_down'} + k_merge"
     ffn = _ffn_kernels(cfg, n_tok)
-    if pred.startswith("k_xstep"):
-        # the matrix-core predictor also lists the union; an fp16 FFN over
-        # one token tile reuses the predictor's step-major copy of x
+    if pred.startswith("k_mp1"):
+        # the matrix-core predictor also lists the union, and its first
+        # product leaves the step-major copy of x that an fp16 FFN over one
+        # token tile reuses
         if cfg.wtype == "f16" and n_tok <= 64 and ffn.startswith("k_xstep + "):
             ffn = ffn[len("k_xstep + "):]
         return f"{pred} (+ list) + {ffn}"
