@@ -1447,6 +1447,122 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
   }
 }
 
+// 8 rows x 4 fp16 columns (each row's 4 columns in one u32x2) -> 4 B
+// operands of 8 rows each, as transpose8x8 does for 8 columns.
+__device__ __forceinline__ void transpose8x4(const u32x2 (&in)[8], u32x4 (&out)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    unsigned o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned lo = j < 2 ? in[2 * m].x : in[2 * m].y, hi = j < 2 ? in[2 * m + 1].x : in[2 * m + 1].y;
+      o[m] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    out[j] = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+// k_mdown_w4 (fp16 rows, 33-64 tokens): k_mdown_wide with 4 columns per lane
+// instead of 8.  Half the accumulators leave room for a second stage of rows
+// in flight (pipeline2, every lane loading: entries past the count or
+// malformed read row 0, columns past d read column 0, both zeroed when the
+// operands are formed), and with 256 columns per workgroup 16 list chunks
+// still give 512 workgroups at the Falcon width, so the partial sums that
+// the merge reads back are half as many bytes as with 32 chunks.
+template <int NB>
+__global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__ w_dt, int d, int d_ff,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ count_ptr, int max_count,
+                                                         const f16* __restrict__ h, int ldh, int nt, int n_chunks,
+                                                         float* __restrict__ part,
+                                                         unsigned long long* __restrict__ rows_read) {
+  constexpr int CPL = 4;
+  constexpr int HU = kMwPiece * 32 / 8;       // 16-byte units of one token's H in a piece
+  constexpr int HS = HU + 1;                  // per-token stride in LDS: tokens on different banks
+  __shared__ u32x4 h_l[16 * NB * HS];
+  __shared__ int rows_l[kMwPiece * 32];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int g = lane >> 4, n16 = lane & 15;
+  const int cnt = clamp_count(count_ptr, max_count);
+  const int ksteps = (cnt + 31) / 32;
+  const int c = blockIdx.y;
+  const int kc0 = (int)((long long)c * ksteps / n_chunks), kc1 = (int)((long long)(c + 1) * ksteps / n_chunks);
+  if (rows_read && blockIdx.x == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
+    const int r0 = kc0 * 32 < cnt ? kc0 * 32 : cnt, r1 = kc1 * 32 < cnt ? kc1 * 32 : cnt;
+    if (r1 > r0) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
+  }
+  const int col = (blockIdx.x * kMdWaves + wave) * 16 * CPL + n16 * CPL;
+  const bool cv = col < d;
+  const int colc = cv ? col : 0;
+
+  f32x4 acc[CPL][NB];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Stage {
+    u32x2 v[8];
+    bool ok[8];
+    int q;
+  };
+  auto load_rows = [&](Stage& S, int q) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = rows_l[q * 32 + g * 8 + r];
+      S.ok[r] = cv && i >= 0;
+      S.v[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2*>(w_dt + (size_t)(S.ok[r] ? i : 0) * d + colc));
+    }
+    S.q = q;
+  };
+  auto mul_rows = [&](const Stage& S) {
+    u32x4 a[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) a[nb] = h_l[(nb * 16 + n16) * HS + S.q * 4 + g];
+    u32x2 rw[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rw[r] = S.ok[r] ? S.v[r] : u32x2{0, 0};
+    u32x4 bt[CPL];
+    transpose8x4(rw, bt);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[j][nb] = mfma(a[nb], bt[j], acc[j][nb]);
+  };
+
+  for (int pb = kc0; pb < kc1; pb += kMwPiece) {
+    const int np = kc1 - pb < kMwPiece ? kc1 - pb : kMwPiece;
+    __syncthreads();                           // the previous piece is no longer read
+    for (int e = threadIdx.x; e < np * 32; e += kMdThreads) {
+      const int p = pb * 32 + e;
+      const int i = p < cnt ? idx[p] : -1;
+      rows_l[e] = (unsigned)i < (unsigned)d_ff ? i : -1;   // past the count or malformed: adds nothing
+    }
+    for (int e = threadIdx.x; e < 16 * NB * np * 4; e += kMdThreads) {
+      const int t = e / (np * 4), u = e - t * (np * 4);
+      const int p = pb * 32 + u * 8;
+      h_l[t * HS + u] = p < cnt ? ld16(h + (size_t)t * ldh + p) : u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    Stage S0, S1;
+    pipeline2(0, np, S0, S1, load_rows, mul_rows);
+  }
+
+  if (cv) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = nb * 16 + 4 * g + i;
+        if (t < nt)
+          *reinterpret_cast<f32x4*>(part + ((size_t)c * nt + t) * d + col) =
+              f32x4{acc[0][nb][i], acc[1][nb][i], acc[2][nb][i], acc[3][nb][i]};
+      }
+  }
+}
+
 // k_mp2_wide (33-64 tokens): the second product with t_hi and t_lo staged in
 // LDS.  k_mp2 re-reads both from the cache for every 64 rows, as many bytes
 // as the p2 rows themselves at 64 tokens.  Here a workgroup of 8 waves owns
@@ -1650,7 +1766,10 @@ template <typename WF>
 constexpr int wide_from() { return std::is_same<WF, Q4>::value ? 2 : 3; }
 int wide_nb(int wtype) { return wtype == 2 ? 2 : 3; }
 
-int mfma_chunks(int wtype, int nb) { return nb >= wide_nb(wtype) ? 32 : (wtype == 2 ? 16 : 8); }
+int mfma_chunks(int wtype, int nb) {
+  if (nb >= wide_nb(wtype)) return wtype == 2 ? 32 : 16;   // fp16: k_mdown_w4, 256 columns per workgroup
+  return wtype == 2 ? 16 : 8;
+}
 
 // k splits of the predictor's first product: about 4 steps of 128 per split.
 int pred_splits(int d) {
@@ -1736,7 +1855,12 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
   constexpr int CPL = down_cpl<WF>(NB);
   const int chunks = mfma_chunks(a.wtype, NB);
   const size_t so = std::is_same<WF, Q4>::value ? (size_t)a.d_ff * (a.d / 32) * 16 : 0;
-  if constexpr (NB >= wide_from<WF>()) {
+  if constexpr (NB >= wide_from<WF>() && std::is_same<WF, f16>::value) {
+    const int tile = kMdWaves * 16 * 4;
+    const dim3 grid((a.d + tile - 1) / tile, chunks);
+    hipLaunchKernelGGL((k_mdown_w4<NB>), grid, dim3(kMdThreads), 0, s, static_cast<const f16*>(a.w_down_t), a.d,
+                       a.d_ff, a.idx, a.count, a.max_count, h, ldh, nt, chunks, a.part, a.rows_read);
+  } else if constexpr (NB >= wide_from<WF>()) {
     const int tile = kMdWaves * 16 * CPL;
     const dim3 grid((a.d + tile - 1) / tile, chunks);
     hipLaunchKernelGGL((k_mdown_wide<WF, NB, CPL>), grid, dim3(kMdThreads), 0, s, a.w_down_t, so, a.d, a.d_ff, a.idx,
