@@ -262,7 +262,8 @@ def _ffn_kernels(cfg, n_tok):
     mfma_from = 3 if cfg.wtype == "f16" else _tile(cfg) + 1
     if n_tok >= mfma_from and cfg.wtype in ("f16", "q4_0") and cfg.d_model % 128 == 0:
         wide = min(n_tok, 64) > 32
-        return f"k_xstep + {'k_mup_wide + k_mfin + k_mdown_wide' if wide else 'k_mup + k_mdown'} + k_merge"
+        down_wide = "k_mdown_w4" if cfg.wtype == "f16" else "k_mdown_wide"
+        return f"k_xstep + {'k_mup_wide + k_mfin + ' + down_wide if wide else 'k_mup + k_mdown'} + k_merge"
     return f"k_up + {'k_down_q4' if q4 else 'k_down'} + k_merge"
 
 
