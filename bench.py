@@ -446,6 +446,18 @@ def main(argv=None):
                 for view, rb in matrix_rows(cfg, layers[li], k):
                     pi.gather_read(view, idx[li], cnt[li:li + 1], row_bytes=rb, max_count=f, out=gr_out)
     sp_rows0 = pi.read_down_rows(ws_s, stream)
+    # the dense-stream floor of the predictor: p1 and p2 of every layer read
+    # with no arithmetic (pi_stream_read), each its own launch as in k_pred1 / k_pred2
+    g_r1, g_r2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_r1, stream=stream):
+        for li in range(L):
+            pi.stream_read(layers[li]["p1"], gr_out)
+    with torch.cuda.graph(g_r2, stream=stream):
+        for li in range(L):
+            pi.stream_read(layers[li]["p2"], gr_out)
+    with torch.cuda.stream(stream):
+        ms_r1 = _time_graph(g_r1, args.reps, stream) / L
+        ms_r2 = _time_graph(g_r2, args.reps, stream) / L
     with torch.cuda.stream(stream):
         ms_pred = _time_graph(g_pred, args.reps, stream) / L
         ms_comp = _time_graph(g_comp, args.reps, stream) / L
@@ -502,6 +514,13 @@ def main(argv=None):
     parts["gather_read"] = {"what": "pi_gather_read of every listed row of every weight matrix, no arithmetic",
                             "avg_us_per_layer": round(ms_gr * 1e3, 3), "bytes_per_layer": int(b_listed),
                             "gbps": gather_read_gbps}
+    b_p1 = layers[0]["p1"].numel() * layers[0]["p1"].element_size()
+    b_p2 = layers[0]["p2"].numel() * layers[0]["p2"].element_size()
+    parts["predictor_read"] = {"what": "pi_stream_read of p1, and separately of p2, of every layer, no arithmetic",
+                               "p1_us_per_layer": round(ms_r1 * 1e3, 3), "p1_bytes": b_p1,
+                               "p1_gbps": round(b_p1 / (ms_r1 * 1e-3) / 1e9, 1),
+                               "p2_us_per_layer": round(ms_r2 * 1e3, 3), "p2_bytes": b_p2,
+                               "p2_gbps": round(b_p2 / (ms_r2 * 1e-3) / 1e9, 1)}
 
     out = {
         "metric": METRIC if B == 1 else METRIC.replace("(batch 1)", f"(batch {B})"),
