@@ -1651,18 +1651,20 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
       }
     };
     auto piece = [&](int p0, auto has_next) {
-      static_assert(kMpPiece == 4, "the unrolled piece is 4 steps");
+      static_assert(kMpPiece == 4 || kMpPiece == 2, "the unrolled piece is 2 or 4 steps");
       rows(S1, p0 + 1);
-      step(S0, 0);
-      rows(S0, p0 + 2);
-      step(S1, 1);
-      rows(S1, p0 + 3);
-      step(S0, 2);
+      if constexpr (kMpPiece == 4) {
+        step(S0, 0);
+        rows(S0, p0 + 2);
+        step(S1, 1);
+        rows(S1, p0 + 3);
+      }
+      step(S0, kMpPiece - 2);
       if constexpr (decltype(has_next)::value) {
         t_load(p0 + kMpPiece);
         rows(S0, p0 + kMpPiece);
       }
-      step(S1, 3);
+      step(S1, kMpPiece - 1);
       if constexpr (decltype(has_next)::value) {
         __syncthreads();                               // every wave is done with this piece's t
         t_store();
