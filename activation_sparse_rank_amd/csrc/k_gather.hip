@@ -826,7 +826,7 @@ bool x_in_lds(int nt_tmpl, int d) { return (size_t)nt_tmpl * d * sizeof(X) <= 32
 template <typename WF, int ACT, int NT>
 hipError_t launch_up(const SparseArgs& a, const typename FfnTraits<WF>::X* x, int nt, hipStream_t s) {
   using X = typename FfnTraits<WF>::X;
-  const int max_waves = 3072;   // about 12 resident waves per CU on 256 CUs
+  const int max_waves = 4096;   // 16 resident waves per CU on 256 CUs: one row per wave up to 4096 rows
   int waves = a.max_count < max_waves ? a.max_count : max_waves;
   if (waves < 1) waves = 1;
   const int grid = (waves + kUpWaves - 1) / kUpWaves;
