@@ -305,7 +305,7 @@ def main(argv=None):
 
     order = "none" if args.no_hot_order else args.order
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the sparse FFN is not sharded across GPUs "
+        print("bench.py: runs on one GPU only; the sparse FFN is not sharded across GPUs "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
