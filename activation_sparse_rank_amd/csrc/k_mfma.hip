@@ -1213,7 +1213,7 @@ __device__ void list_marked(const int* __restrict__ uni, int base, int d_ff, uns
 // (fp32), and its fp16 split t_hi = fp16(t), t_lo = fp16(t - t_hi), stored
 // step-major ([rank/128][nt][128]) for k_mp2.
 // It also clears zero_n words at zero_ptr and the word at fault (the list
-// counters of k_mp2 / k_mp2_wide in the same call); NULL skips them.  A t_hi
+// counters of k_mp2 in the same call); NULL skips them.  A t_hi
 // that is not finite in fp16 raises PI_FLAG_FP16_RANGE in *flags.
 __global__ __launch_bounds__(256) void k_tsplit(const float* __restrict__ part, int n_split, int nt, int rank,
                                                 float* __restrict__ t, f16* __restrict__ th, f16* __restrict__ tl,
@@ -1241,104 +1241,6 @@ __global__ __launch_bounds__(256) void k_tsplit(const float* __restrict__ part, 
   const size_t o = ((size_t)(r / kMuK) * nt + j) * kMuK + r % kMuK;     // step-major, as TokStep reads
   th[o] = hi;
   tl[o] = (f16)(sum - (float)hi);
-}
-
-template <int NB>
-__global__ __launch_bounds__(kMuThreads) void k_mp2(const f16* __restrict__ p2, const float* __restrict__ c,
-                                                    const f16* __restrict__ th, const f16* __restrict__ tl, int rank,
-                                                    int d_ff, int nt, float theta, uint8_t* __restrict__ mask,
-                                                    float* __restrict__ logits, uint8_t* __restrict__ umask,
-                                                    int umask_first, unsigned* __restrict__ status,
-                                                    int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                                                    unsigned* __restrict__ hdr, unsigned* __restrict__ fault) {
-  constexpr int NQ = kMuMB * NB;
-  __shared__ float red[kMuWaves][NQ][4][kWave];
-  __shared__ int uni[kMuRows];                 // union over the tile's tokens
-  __shared__ int wl[kMuWaves];
-  if (threadIdx.x < kMuRows) uni[threadIdx.x] = 0;
-  const int lane = lane_id(), wave = wave_id();
-  const int g = lane >> 4, n16 = lane & 15;
-  const int r0 = blockIdx.x * kMuRows;
-  int row[kMuMB];
-  bool rv[kMuMB];
-#pragma unroll
-  for (int mb = 0; mb < kMuMB; ++mb) {
-    row[mb] = r0 + mb * 16 + n16;
-    rv[mb] = row[mb] < d_ff;
-  }
-  f32x4 acc[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ns = rank / kMuK;
-  const int s0 = wave * ns / kMuWaves, s1 = (wave + 1) * ns / kMuWaves;
-#pragma unroll
-  for (int mb = 0; mb < kMuMB; ++mb) row[mb] = rv[mb] ? row[mb] : 0;
-  // (every lane loading, as in k_mp1, made this kernel 0.7 us slower per
-  // Falcon layer at 8 tokens: its loads stay conditional)
-  struct Step {
-    RowStep<f16, kMuMB> w;
-    TokStep<NB> hi, lo;
-  };
-  auto load = [&](Step& S, int st) {
-    S.w.load(p2, 0, row, rv, rank, st * kMuK, g);
-    S.hi.load(th, nt, st, g, n16);
-    S.lo.load(tl, nt, st, g, n16);
-  };
-  auto mul = [&](const Step& S) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int mb = 0; mb < kMuMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.hi.v[nb][s], acc[mb * NB + nb]);
-          acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.lo.v[nb][s], acc[mb * NB + nb]);
-        }
-  };
-  if constexpr (NB <= 2) {
-    Step S0, S1;
-    pipeline2(s0, s1, S0, S1, load, mul);
-  } else {
-    for (int st = s0; st < s1; ++st) {
-      Step S;
-      load(S, st);
-      mul(S);
-    }
-  }
-  float sum[NB][4];
-  sum_waves<NQ>(&red[0][0][0][0], acc, sum);
-  const int ol = threadIdx.x & (kWave - 1), oq = threadIdx.x >> 6;
-#pragma unroll
-  for (int e = 0; e < NB; ++e) {
-    const int q = oq + 4 * e;
-    const int mb = q / NB, nb = q % NB;
-    const int j = nb * 16 + (ol & 15);
-    const int r = r0 + mb * 16 + 4 * (ol >> 4);
-    if (j < nt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (r + i < d_ff) {
-          const float l = sum[e][i] + c[r + i];
-          if (mask) mask[(size_t)j * d_ff + r + i] = l > theta ? 1 : 0;
-          if (logits) logits[(size_t)j * d_ff + r + i] = l;
-          if (l > theta) uni[r + i - r0] = 1;    // every writer stores the same value
-        }
-      }
-    }
-  }
-  if (umask) {
-    __syncthreads();
-    const int i = threadIdx.x;
-    if (i < kMuRows && r0 + i < d_ff) {
-      const int u = uni[i] | (umask_first ? 0 : umask[r0 + i]);
-      umask[r0 + i] = (uint8_t)u;
-      uni[i] = u;
-    }
-    if (idx) {
-      __syncthreads();
-      list_marked<kMuThreads, kMuRows>(uni, r0, d_ff, status, idx, count, wl, hdr, fault);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1563,19 +1465,26 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
   }
 }
 
-// k_mp2_wide (33-64 tokens): the second product with t_hi and t_lo staged in
-// LDS.  k_mp2 re-reads both from the cache for every 64 rows, as many bytes
-// as the p2 rows themselves at 64 tokens.  Here a workgroup of 8 waves owns
-// 128 rows (16 per wave), walks all of k itself (one accumulator per token
+// k_mp2: the second product with t_hi and t_lo staged in LDS (read from
+// the cache once per workgroup, not once per 16-row block: at 64 tokens as
+// many bytes as the p2 rows themselves).  A workgroup of 8 waves owns 128
+// rows (16 per wave), walks all of k itself (one accumulator per token
 // block, no cross-wave sum), and stages kMpPiece k steps of t_hi and t_lo
-// per piece; each wave keeps the next step's p2 rows in flight (a whole
+// per piece.  With 1-2 token blocks (up to 32 tokens) the p2 rows are loaded
+// in the transposed pattern (RowStepTU: 256 contiguous bytes of a row per
+// 16 lanes) and two steps of rows stay in flight while two are multiplied;
+// with 3-4 blocks the LDS holds no buffer for that, the rows are loaded in
+// the operand pattern, and each wave keeps the next step in flight (a whole
 // piece in flight was slower: the staging loads then queue behind it).
+// Measured at Falcon shape against a 4-wave form that split k over the
+// waves and re-read t per step (predictor, stand-alone call): 4 tokens
+// 24.0 -> 22.5 us, 8 tokens 24.7 -> 22.8 us, 24 tokens 37.2 -> 27.7 us.
 constexpr int kMpThreads = 512;
 constexpr int kMpRows = kMpThreads / kWave * 16;
 constexpr int kMpPiece = 4;
 
 template <int NB>
-__global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__ p2, const float* __restrict__ c,
+__global__ __launch_bounds__(kMpThreads) void k_mp2(const f16* __restrict__ p2, const float* __restrict__ c,
                                                          const f16* __restrict__ th, const f16* __restrict__ tl,
                                                          int rank, int d_ff, int nt, float theta,
                                                          uint8_t* __restrict__ mask, float* __restrict__ logits,
@@ -1630,10 +1539,29 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
         tl_l[q][u] = r < su ? lr[k] : u32x4{0, 0, 0, 0};
       }
     };
+    // p2 rows in the transposed pattern (256 contiguous bytes of a row per
+    // 16 lanes), moved into the operand layout through this wave's LDS buffer
+    // (1-2 token blocks; more leave no LDS for the buffers)
+    constexpr bool TU = NB <= 2;
+    __shared__ u32x4 w_l[TU ? kMpThreads / kWave : 1][TU ? 16 * kTStride : 1];
+    int rowt[1][4];
+    bool rvt[1][4];
+    rows_for_load<1>(row, rv, lane, rowt, rvt);
     bool all[1] = {true};
-    RowStep<f16, 1> S0, S1;
-    auto rows = [&](RowStep<f16, 1>& S, int st) { S.load(p2, 0, row, all, rank, st * kMuK, g); };
-    auto step = [&](const RowStep<f16, 1>& S, int q) {
+    using Rows = typename std::conditional<TU, RowStepTU<1>, RowStep<f16, 1>>::type;
+    Rows S0, S1;
+    auto rows = [&](Rows& S, int st) {
+      if constexpr (TU)
+        S.load(p2, rowt, rank, st * kMuK, lane);
+      else
+        S.load(p2, 0, row, all, rank, st * kMuK, g);
+    };
+    auto step = [&](const Rows& S, int q) {
+      u32x4 a[4];
+      if constexpr (TU)
+        S.operands(0, rvt, &w_l[TU ? wave : 0][0], lane, a);
+      else
+        S.operands(0, a);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 bh[NB], bl[NB];
@@ -1645,8 +1573,8 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          acc[nb] = mfma(S.v[0][s], bh[nb], acc[nb]);
-          acc[nb] = mfma(S.v[0][s], bl[nb], acc[nb]);
+          acc[nb] = mfma(a[s], bh[nb], acc[nb]);
+          acc[nb] = mfma(a[s], bl[nb], acc[nb]);
         }
       }
     };
@@ -1671,13 +1599,46 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2_wide(const f16* __restrict__
         __syncthreads();
       }
     };
+    // 1-2 token blocks (one workgroup per CU at Falcon shape, registers to
+    // spare): stages of two steps, so two steps of rows are in flight while
+    // two are multiplied
+    Rows D0[2], D1[2];
+    auto piece2 = [&](int p0, auto has_next) {
+      static_assert(kMpPiece == 4, "two stages of two steps");
+      rows(D1[0], p0 + 2);
+      rows(D1[1], p0 + 3);
+      step(D0[0], 0);
+      step(D0[1], 1);
+      if constexpr (decltype(has_next)::value) {
+        t_load(p0 + kMpPiece);
+        rows(D0[0], p0 + kMpPiece);
+        rows(D0[1], p0 + kMpPiece + 1);
+      }
+      step(D1[0], 2);
+      step(D1[1], 3);
+      if constexpr (decltype(has_next)::value) {
+        __syncthreads();                               // every wave is done with this piece's t
+        t_store();
+        __syncthreads();
+      }
+    };
     t_load(0);
-    rows(S0, 0);
+    if constexpr (TU) {
+      rows(D0[0], 0);
+      rows(D0[1], 1);
+    } else {
+      rows(S0, 0);
+    }
     t_store();
     __syncthreads();
     int p0 = 0;
-    for (; p0 + kMpPiece < ns; p0 += kMpPiece) piece(p0, std::true_type{});
-    piece(p0, std::false_type{});
+    if constexpr (TU) {
+      for (; p0 + kMpPiece < ns; p0 += kMpPiece) piece2(p0, std::true_type{});
+      piece2(p0, std::false_type{});
+    } else {
+      for (; p0 + kMpPiece < ns; p0 += kMpPiece) piece(p0, std::true_type{});
+      piece(p0, std::false_type{});
+    }
   }
   for (int p0 = 0; p0 < ns && !whole; p0 += kMpPiece) {
     const int np = ns - p0 < kMpPiece ? ns - p0 : kMpPiece;
@@ -1924,7 +1885,7 @@ hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (xs_out) *xs_out = xs;
-  const int grid2 = NB >= 3 ? (d_ff + kMpRows - 1) / kMpRows : (d_ff + kMuRows - 1) / kMuRows;
+  const int grid2 = (d_ff + kMpRows - 1) / kMpRows;
   const bool list = pl.idx != nullptr && umask != nullptr;
   if (list && (pl.status == nullptr || pl.count == nullptr || pl.hdr == nullptr || pl.fault == nullptr ||
                grid2 > pl.n_status))
@@ -1940,12 +1901,8 @@ hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x,
   int32_t* li = list ? pl.idx : nullptr;
   int32_t* lc = list ? pl.count : nullptr;
   unsigned* fl = list ? pl.fault : nullptr;
-  if constexpr (NB >= 3)
-    hipLaunchKernelGGL((k_mp2_wide<NB>), dim3(grid2), dim3(kMpThreads), 0, s, p2, c, th, tl, rank, d_ff, nt, theta,
-                       mask, logits, umask, first, st, li, lc, pl.hdr, fl);
-  else
-    hipLaunchKernelGGL((k_mp2<NB>), dim3(grid2), dim3(kMuThreads), 0, s, p2, c, th, tl, rank, d_ff, nt, theta, mask,
-                       logits, umask, first, st, li, lc, pl.hdr, fl);
+  hipLaunchKernelGGL((k_mp2<NB>), dim3(grid2), dim3(kMpThreads), 0, s, p2, c, th, tl, rank, d_ff, nt, theta, mask,
+                     logits, umask, first, st, li, lc, pl.hdr, fl);
   return hipGetLastError();
 }
 

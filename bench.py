@@ -252,7 +252,7 @@ def matrix_rows(cfg, lw, key):
 def _pred_kernels(cfg, n_tok):
     """Kernels of one pi_predict call (labels only)."""
     if cfg.pred_wtype == "f16" and cfg.d_model % 128 == 0 and cfg.rank % 128 == 0 and n_tok > 2:
-        return f"k_mp1 + k_tsplit + {'k_mp2_wide' if min(n_tok, 64) > 32 else 'k_mp2'}"
+        return "k_mp1 + k_tsplit + k_mp2"
     return "k_pred1 + k_pred2"
 
 
