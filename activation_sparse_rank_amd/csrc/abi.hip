@@ -129,7 +129,7 @@ hipError_t predict_any(const pi_predictor* pred, const void* x, int n_tok, float
   if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok))
     return pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
                                    theta, t, ws + L.tpart, mask, logits, nullptr, nullptr, 0, nullptr, nullptr,
-                                   reinterpret_cast<unsigned*>(ws), nullptr, nullptr, s);
+                                   reinterpret_cast<unsigned*>(ws), nullptr, false, nullptr, s);
   hipError_t e = pi::launch_predict_stage1(pred->wtype, pred->p1, x, n_tok, pred->d_model, pred->rank, t, nullptr,
                                            0, s);
   if (e != hipSuccess) return e;
@@ -218,12 +218,12 @@ pi_status run_layer(const pi_predictor* pred, const pi_ffn* ffn, const void* x, 
   // Many tokens: predict every token, take the union list, then the list path.
   if (pi::pred_mfma_path(pred->wtype, pred->d_model, pred->rank, n_tok)) {
     // The matrix-core predictor writes the union mask and lists it (idx,
-    // count) in its last kernel; the fp16 FFN reuses its step-major copy
-    // of a single token tile.
+    // count) in its last kernel; the FFN reuses its step-major copy of a
+    // single token tile (in block order for Q4_0 rows).
     const void* xs = nullptr;
     e = pi::launch_predict_mfma(pred->p1, pred->p2, pred->c, x, n_tok, pred->d_model, pred->rank, pred->d_ff,
                                 theta_of(tau), t, w + L.tpart, nullptr, nullptr, mask, status, L.n_segments, idx,
-                                count, hdr, fault, &xs, s);
+                                count, hdr, fault, ffn->wtype == PI_Q4_0, &xs, s);
     a.xs_pre = xs;
     a.fault = fault;
   } else {

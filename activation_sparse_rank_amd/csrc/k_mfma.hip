@@ -332,15 +332,18 @@ struct TokStepRM {
       ld_k128(x + (size_t)(t < nt ? t : nt - 1) * d + (size_t)st * kMuK, true, g, false, v[nb]);
     }
   }
-  // xs[st][t][32s + 8g .. +8] = the lane's operand of sub-step s (natural order)
-  __device__ __forceinline__ void store_step(f16* xs, int nt, int st, int g, int n16) const {
+  // xs[st][t][32s + 8g .. +8] = the lane's operand of sub-step s (natural
+  // order), or with block (operands meeting Q4_0 rows, as k_xstep<true>
+  // writes them) xs[st][t][32g + 8s .. +8]
+  __device__ __forceinline__ void store_step(f16* xs, int nt, int st, int g, int n16, bool block) const {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int t = nb * 16 + n16;
       if (t < nt) {
-        f16* dst = xs + ((size_t)st * nt + t) * kMuK + 8 * g;
+        f16* dst = xs + ((size_t)st * nt + t) * kMuK;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(dst + 32 * s) = v[nb][s];
+        for (int s = 0; s < 4; ++s)
+          *reinterpret_cast<u32x4*>(dst + (block ? 32 * g + 8 * s : 32 * s + 8 * g)) = v[nb][s];
       }
     }
   }
@@ -1078,9 +1081,10 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
 template <int NB>
 __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, const f16* __restrict__ x, int d,
                                                     int rank, int nt, float* __restrict__ part,
-                                                    f16* __restrict__ xs) {
+                                                    f16* __restrict__ xs, int xs_block) {
   // x: the row-major token tile; the workgroups of row block 0 also write
-  // the step-major copy xs (nullable) of the steps they read
+  // the step-major copy xs (nullable) of the steps they read, in block order
+  // when xs_block (for a Q4_0 FFN)
   constexpr int NQ = kMuMB * NB;
   __shared__ float red[kMuWaves][NQ][4][kWave];
   const int lane = lane_id(), wave = wave_id();
@@ -1124,7 +1128,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, 
       for (int mb = 0; mb < kMuMB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.x.v[nb][s], acc[mb * NB + nb]);
-    if (copy) S.x.store_step(xs, nt, S.st, g, n16);
+    if (copy) S.x.store_step(xs, nt, S.st, g, n16, xs_block != 0);
   };
   Step S0, S1;
   pipeline2(s0, s1, S0, S1, load, mul);
@@ -1797,7 +1801,7 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
   f16* h = reinterpret_cast<f16*>(a.h);
   const int ldh = ldh_of(a.d_ff);
   hipError_t e;
-  if (!std::is_same<WF, Q4>::value && a.xs_pre != nullptr && t0 == 0 && nt == a.n_tok) {
+  if (a.xs_pre != nullptr && t0 == 0 && nt == a.n_tok) {
     x = static_cast<const f16*>(a.xs_pre);          // the predictor's step-major copy of the same tile
   } else {
     f16* xs = reinterpret_cast<f16*>(reinterpret_cast<char*>(a.h) + h_region(a.d_ff, 4));
@@ -1874,14 +1878,14 @@ struct PredList {
 template <int NB>
 hipError_t run_ptile(const f16* p1, const f16* p2, const float* c, const f16* x, int nt, int d, int rank, int d_ff,
                      float theta, float* t, char* ws, uint8_t* mask, float* logits, uint8_t* umask, int first,
-                     const PredList& pl, const f16** xs_out, hipStream_t s) {
+                     const PredList& pl, bool xs_block, const f16** xs_out, hipStream_t s) {
   const int splits = pred_splits(d);
   float* part = reinterpret_cast<float*>(ws);
   f16* th = reinterpret_cast<f16*>(ws + up256((size_t)splits * kMfmaTile * rank * sizeof(float)));
   f16* tl = th + (size_t)kMfmaTile * rank;
   f16* xs = tl + (size_t)kMfmaTile * rank;
   hipLaunchKernelGGL((k_mp1<NB>), dim3((rank + kMuRows - 1) / kMuRows, splits), dim3(kMuThreads), 0, s, p1, x, d,
-                     rank, nt, part, xs);
+                     rank, nt, part, xs, xs_block ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (xs_out) *xs_out = xs;
@@ -1950,7 +1954,7 @@ size_t pred_mfma_part_bytes(int d, int rank, int) {
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
                                uint8_t* umask, unsigned* status, int n_status, int32_t* idx, int32_t* count,
-                               unsigned* hdr, unsigned* fault, const void** xs_out, hipStream_t s) {
+                               unsigned* hdr, unsigned* fault, bool xs_block, const void** xs_out, hipStream_t s) {
   if (xs_out) *xs_out = nullptr;
   for (int t0 = 0; t0 < n_tok; t0 += kMfmaTile) {
     const int nt = n_tok - t0 < kMfmaTile ? n_tok - t0 : kMfmaTile;
@@ -1967,13 +1971,13 @@ hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, c
     char* wsp = static_cast<char*>(ws);
     hipError_t e;
     if (nt <= 16)
-      e = run_ptile<1>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
+      e = run_ptile<1>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, xs_block, &xs, s);
     else if (nt <= 32)
-      e = run_ptile<2>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
+      e = run_ptile<2>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, xs_block, &xs, s);
     else if (nt <= 48)
-      e = run_ptile<3>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
+      e = run_ptile<3>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, xs_block, &xs, s);
     else
-      e = run_ptile<4>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, &xs, s);
+      e = run_ptile<4>(a, b, c, xt, nt, d, rank, d_ff, theta, tt, wsp, mt, lt, umask, first, pl, xs_block, &xs, s);
     if (e != hipSuccess) return e;
     if (xs_out && t0 == 0 && last) *xs_out = xs;     // one tile: its step-major copy stays valid
   }

@@ -150,8 +150,10 @@ struct SparseArgs {
   float* h;                 // workspace [tile][d_ff] fp32, by list position
   float* part;              // workspace [n_chunks][tile][d] fp32
   int n_chunks, n_slices;
-  // Matrix-core path, fp16 weights, one token tile: x already copied
-  // step-major ([d/128][n_tok][128] fp16) by the predictor; NULL: copy it.
+  // Matrix-core path, one token tile: x already copied step-major
+  // ([d/128][n_tok][128] fp16; for Q4_0 weights in block order, as
+  // launch_predict_mfma writes it with xs_block) by the predictor; NULL:
+  // copy it.
   const void* xs_pre = nullptr;
   // Sticky flags word (PI_FLAG_FP16_RANGE from the matrix-core H); nullable.
   unsigned* flags = nullptr;
@@ -201,7 +203,8 @@ hipError_t launch_sparse_ffn_mfma(const SparseArgs& a, hipStream_t s);
 // may be NULL; umask (nullable): [d_ff], 1 where any token is active.
 // With umask and idx given, the union is also listed (ascending) into idx
 // and count, using status[n_status] as counters (cleared in the call).
-// xs_out (nullable) receives the step-major token copy when n_tok <= 64.
+// xs_out (nullable) receives the step-major token copy when n_tok <= 64; with
+// xs_block its 16-byte groups are in the block order Q4_0 rows meet.
 bool pred_mfma_path(int wtype, int d, int rank, int n_tok);
 size_t pred_mfma_part_bytes(int d, int rank, int n_tok);
 // hdr: the workspace header (flags; the wait hooks when listing); fault: the
@@ -210,7 +213,7 @@ size_t pred_mfma_part_bytes(int d, int rank, int n_tok);
 hipError_t launch_predict_mfma(const void* p1, const void* p2, const float* c, const void* x, int n_tok, int d,
                                int rank, int d_ff, float theta, float* t, void* ws, uint8_t* mask, float* logits,
                                uint8_t* umask, unsigned* status, int n_status, int32_t* idx, int32_t* count,
-                               unsigned* hdr, unsigned* fault, const void** xs_out, hipStream_t s);
+                               unsigned* hdr, unsigned* fault, bool xs_block, const void** xs_out, hipStream_t s);
 
 // y = sum over c of part[c][0 .. n), in chunk order (fp32 or fp16 out); NaN
 // everywhere when fault (nullable) holds a nonzero word.
