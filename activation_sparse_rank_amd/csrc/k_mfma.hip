@@ -1107,27 +1107,46 @@ __global__ __launch_bounds__(kMuThreads) void k_mp1(const f16* __restrict__ p1, 
 #pragma unroll
   for (int mb = 0; mb < kMuMB; ++mb) row[mb] = rv[mb] ? row[mb] : 0;
   const bool copy = xs != nullptr && blockIdx.x == 0;
-  // every lane loads (rows past rank read row 0; their sums are never stored)
+  // every lane loads (rows past rank read row 0; their sums are never stored).
+  // With 1-2 token blocks the p1 rows are loaded in the transposed pattern
+  // (RowStepTU: 256 contiguous bytes of a row per 16 lanes) and moved into
+  // the operand layout through this wave's LDS buffer; more blocks leave no
+  // registers for it and load the operand pattern (64 bytes of 16 rows).
+  constexpr bool TU = NB <= 2;
+  __shared__ u32x4 w_l[TU ? kMuWaves : 1][TU ? 16 * kTStride : 1];
+  int rowt[kMuMB][4];
+  bool rvt[kMuMB][4];
   bool all[kMuMB];
 #pragma unroll
   for (int mb = 0; mb < kMuMB; ++mb) all[mb] = true;
+  if constexpr (TU) rows_for_load<kMuMB>(row, all, lane, rowt, rvt);
+  using Rows = typename std::conditional<TU, RowStepTU<kMuMB>, RowStep<f16, kMuMB>>::type;
   struct Step {
-    RowStep<f16, kMuMB> w;
+    Rows w;
     TokStepRM<NB> x;
     int st;
   };
   auto load = [&](Step& S, int st) {
-    S.w.load(p1, 0, row, all, d, st * kMuK, g);
+    if constexpr (TU)
+      S.w.load(p1, rowt, d, st * kMuK, lane);
+    else
+      S.w.load(p1, 0, row, all, d, st * kMuK, g);
     S.x.load(x, d, nt, st, g, n16);
     S.st = st;
   };
   auto mul = [&](const Step& S) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int mb = 0; mb < kMuMB; ++mb) {
+      u32x4 a[4];
+      if constexpr (TU)
+        S.w.operands(mb, rvt, &w_l[TU ? wave : 0][0], lane, a);
+      else
+        S.w.operands(mb, a);
 #pragma unroll
-      for (int mb = 0; mb < kMuMB; ++mb)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb * NB + nb] = mfma(S.w.v[mb][s], S.x.v[nb][s], acc[mb * NB + nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[mb * NB + nb] = mfma(a[s], S.x.v[nb][s], acc[mb * NB + nb]);
+    }
     if (copy) S.x.store_step(xs, nt, S.st, g, n16, xs_block != 0);
   };
   Step S0, S1;
