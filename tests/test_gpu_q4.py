@@ -182,3 +182,14 @@ def test_layer_q4_model_shape(name):
     # two tokens: the fused kernel's Q4_0 tile of 2 (x of both tokens in LDS)
     _layer_check(dl, n_tok=2, stream_id=2, what=f"{name} b2")
     _layer_check(dl, n_tok=8, rows=[0, 5, 7], stream_id=1, what=f"{name} b8")
+
+
+@pytest.mark.parametrize("n_tok", [17, 64])
+def test_layer_q4_wide(n_tok):
+    # Many tokens: the matrix-core predictor leaves the token tile in the
+    # block order Q4_0 rows meet, and the wide FFN kernels read that copy;
+    # the separate calls copy the tokens themselves.  Both must give the
+    # same bits, and the sampled tokens must match the oracle.
+    cfg = workload.get_config("falcon40b_q4")
+    dl = DeviceLayer(cfg, layer=0)
+    _layer_check(dl, n_tok=n_tok, rows=[0, n_tok - 1], stream_id=3, what=f"falcon40b_q4 n={n_tok}")
