@@ -959,6 +959,19 @@ struct DownRows<Q4, CPL> {
   }
 };
 
+// The GPU deals the workgroups of a launch to its 8 XCDs round-robin by
+// linear index (x fastest), and each XCD has its own L2.  This renumbers a
+// 2-D grid so that consecutive logical workgroups (x fastest) share an XCD:
+// logical number L = (id % 8) * (total / 8) + id / 8, a bijection when the
+// grid size is a multiple of 8 (otherwise the numbering is left as it is).
+__device__ __forceinline__ void xcd_grouped(int& x, int& y) {
+  const int gx = gridDim.x, total = gx * (int)gridDim.y;
+  const int id = (int)blockIdx.x + gx * (int)blockIdx.y;
+  const int L = total % 8 == 0 ? (id % 8) * (total / 8) + id / 8 : id;
+  x = L % gx;
+  y = L / gx;
+}
+
 template <typename WF, int NB, int CPL>
 __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w_dt, size_t scale_off, int d,
                                                       int d_ff, const int32_t* __restrict__ idx,
@@ -973,14 +986,18 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
   const int g = lane >> 4, n16 = lane & 15;
   const int cnt = clamp_count(count_ptr, max_count);
   const int ksteps = (cnt + 31) / 32;
-  const int c = blockIdx.y;
+  // Q4_0: the 8 column tiles that share a 128-byte line of scales (2048
+  // columns) run on one XCD, so the line is fetched once per XCD, not once
+  // per tile
+  int tile = blockIdx.x, c = blockIdx.y;
+  if constexpr (std::is_same<WF, Q4>::value) xcd_grouped(tile, c);
   const int kc0 = (int)((long long)c * ksteps / n_chunks), kc1 = (int)((long long)(c + 1) * ksteps / n_chunks);
-  if (rows_read && blockIdx.x == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
+  if (rows_read && tile == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
     const int r0 = kc0 * 32 < cnt ? kc0 * 32 : cnt, r1 = kc1 * 32 < cnt ? kc1 * 32 : cnt;
     if (r1 > r0) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
   }
   const int kw0 = kc0 + wave * (kc1 - kc0) / kMdWaves, kw1 = kc0 + (wave + 1) * (kc1 - kc0) / kMdWaves;
-  const int col = blockIdx.x * 16 * CPL + n16 * CPL;
+  const int col = tile * 16 * CPL + n16 * CPL;
   const bool cv = col < d;
 
   f32x4 acc[CPL][NB];
@@ -1411,13 +1428,15 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
   const int g = lane >> 4, n16 = lane & 15;
   const int cnt = clamp_count(count_ptr, max_count);
   const int ksteps = (cnt + 31) / 32;
-  const int c = blockIdx.y;
+  // the column tiles of a chunk, which all read its H, run on one XCD
+  int tile, c;
+  xcd_grouped(tile, c);
   const int kc0 = (int)((long long)c * ksteps / n_chunks), kc1 = (int)((long long)(c + 1) * ksteps / n_chunks);
-  if (rows_read && blockIdx.x == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
+  if (rows_read && tile == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
     const int r0 = kc0 * 32 < cnt ? kc0 * 32 : cnt, r1 = kc1 * 32 < cnt ? kc1 * 32 : cnt;
     if (r1 > r0) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
   }
-  const int col = (blockIdx.x * kMdWaves + wave) * 16 * CPL + n16 * CPL;
+  const int col = (tile * kMdWaves + wave) * 16 * CPL + n16 * CPL;
   const bool cv = col < d;
   const int colc = cv ? col : 0;
 
