@@ -574,14 +574,23 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
         }
       }
     }
-  } else if constexpr (kPipe) {
-    Step S0, S1;
-    pipeline2(s0, s1, S0, S1, load, mul);
   } else {
-    for (int st = s0; st < s1; ++st) {
-      Step S;
-      load(S, st);
-      mul(S);
+    // The workgroups start their k walk at different steps (workgroup b at
+    // step b % steps of its quarter, wrapping around), as in k_mup_wide:
+    // all of them in step would read the same few hundred bytes of many
+    // rows 16 KB apart at once (Falcon batch-8 FFN 80.7 -> 75.5 us).
+    const int nst = s1 - s0;
+    const int rot = nst > 0 ? (int)(blockIdx.x % (unsigned)nst) : 0;
+    auto load_rot = [&](Step& S, int st) { load(S, s0 + (st - s0 + rot) % nst); };
+    if constexpr (kPipe) {
+      Step S0, S1;
+      pipeline2(s0, s1, S0, S1, load_rot, mul);
+    } else {
+      for (int st = s0; st < s1; ++st) {
+        Step S;
+        load_rot(S, st);
+        mul(S);
+      }
     }
   }
 
@@ -762,8 +771,8 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
             for (int nb = 0; nb < NB; ++nb) au[mb][nb] = mfma(a[mb][s], b[nb], au[mb][nb]);
         }
       };
-      // piece p0 (its x in x_l, the rows of its first step in S0)
-      auto piece = [&](int p0, auto has_next) {
+      // piece p0 (its x in x_l, the rows of its first step in S0); pn: the next piece
+      auto piece = [&](int p0, int pn, auto has_next) {
         static_assert(kMxPiece == 4, "the unrolled piece is 4 steps");
         rows(S1, p0 + 1);
         step(S0, 0);
@@ -772,8 +781,8 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
         rows(S1, p0 + 3);
         step(S0, 2);
         if constexpr (decltype(has_next)::value) {
-          x_load(p0 + kMxPiece);
-          rows(S0, p0 + kMxPiece);
+          x_load(pn);
+          rows(S0, pn);
         }
         step(S1, 3);
         if constexpr (decltype(has_next)::value) {
@@ -782,13 +791,22 @@ __global__ __launch_bounds__(kMxThreads) void k_mup_wide(const void* __restrict_
           __syncthreads();
         }
       };
-      x_load(s0);
-      rows(S0, s0);
+      // The workgroups start at different pieces (row block r at piece
+      // r % pieces, wrapping around): all of them walking k in step would
+      // read the same few hundred bytes of thousands of rows 16 KB apart at
+      // once, which the memory channels serve far below their rate
+      // (Falcon 64-token FFN 217.5 -> 192.5 us).  Each row's sum over k then
+      // runs in that rotated, fixed order.
+      const int npc = (s1 - s0) / kMxPiece;
+      const int rot = (int)(blockIdx.x % (unsigned)npc);
+      auto pstart = [&](int i) { return s0 + ((i + rot) % npc) * kMxPiece; };
+      x_load(pstart(0));
+      rows(S0, pstart(0));
       x_store();
       __syncthreads();
-      int p0 = s0;
-      for (; p0 + kMxPiece < s1; p0 += kMxPiece) piece(p0, std::true_type{});
-      piece(p0, std::false_type{});
+      int i = 0;
+      for (; i + 1 < npc; ++i) piece(pstart(i), pstart(i + 1), std::true_type{});
+      piece(pstart(i), 0, std::false_type{});
     }
   }
   for (int p0 = s0; p0 < s1; p0 += kMxPiece) {
