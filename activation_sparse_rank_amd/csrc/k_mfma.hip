@@ -1529,16 +1529,18 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
 // the cache once per workgroup, not once per 16-row block: at 64 tokens as
 // many bytes as the p2 rows themselves).  A workgroup of 8 waves owns 128
 // rows (16 per wave), walks all of k itself (one accumulator per token
-// block, no cross-wave sum), and stages kMpPiece k steps of t_hi and t_lo
-// per piece.  With 1-2 token blocks (up to 32 tokens) the p2 rows are loaded
-// in the transposed pattern (RowStepTU: 256 contiguous bytes of a row per
-// 16 lanes) and two steps of rows stay in flight while two are multiplied;
-// with 3-4 blocks the LDS holds no buffer for that, the rows are loaded in
-// the operand pattern, and each wave keeps the next step in flight (a whole
-// piece in flight was slower: the staging loads then queue behind it).
-// Measured at Falcon shape against a 4-wave form that split k over the
-// waves and re-read t per step (predictor, stand-alone call): 4 tokens
-// 24.0 -> 22.5 us, 8 tokens 24.7 -> 22.8 us, 24 tokens 37.2 -> 27.7 us.
+// block, no cross-wave sum), and stages a piece of k steps of t_hi and t_lo
+// at a time.  The p2 rows are loaded in the transposed pattern (RowStepTU:
+// 256 contiguous bytes of a row per 16 lanes).  With 1-2 token blocks (up
+// to 32 tokens) the pieces are kMpPiece steps and two steps of rows stay in
+// flight while two are multiplied; with 3-4 blocks the pieces are 2 steps
+// (so that the staged t leaves LDS for the row buffers) and each wave keeps
+// the next step in flight (a whole piece in flight was slower: the staging
+// loads then queue behind it).  Measured at Falcon shape against a 4-wave
+// form that split k over the waves and re-read t per step (predictor,
+// stand-alone call): 4 tokens 24.0 -> 22.5 us, 8 tokens 24.7 -> 22.8 us,
+// 24 tokens 37.2 -> 27.7 us; 64 tokens, operand-pattern rows -> transposed,
+// 41.2 -> 39.8 us.
 constexpr int kMpThreads = 512;
 constexpr int kMpRows = kMpThreads / kWave * 16;
 constexpr int kMpPiece = 4;
@@ -1553,7 +1555,8 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2(const f16* __restrict__ p2, 
                                                          int32_t* __restrict__ count, unsigned* __restrict__ hdr,
                                                          unsigned* __restrict__ fault) {
   constexpr int LU = 16 * NB * kMuK / 8;          // 16-byte units of one step (all token slots)
-  __shared__ u32x4 th_l[kMpPiece][16 * NB * kTokStride], tl_l[kMpPiece][16 * NB * kTokStride];
+  constexpr int PC = NB <= 2 ? kMpPiece : 2;      // k-steps per staged piece
+  __shared__ u32x4 th_l[PC][16 * NB * kTokStride], tl_l[PC][16 * NB * kTokStride];
   __shared__ int uni[kMpRows];                    // union over the tile's tokens
   __shared__ int wl[kMpThreads / kWave];
   if (threadIdx.x < kMpRows) uni[threadIdx.x] = 0;
@@ -1571,13 +1574,13 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2(const f16* __restrict__ p2, 
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ns = rank / kMuK;
   const int su = nt * (kMuK / 8);                 // units of one step of the nt real tokens
-  const bool whole = ns % kMpPiece == 0;
+  const bool whole = ns % PC == 0;
   if (whole) {
     // Whole pieces: the unrolled branch-free pipeline of k_mup_wide.  Every
     // lane loads (rows past d_ff read row 0 and are never stored; token
     // slots past nt read a valid unit and are zeroed in LDS), and the next
     // piece's t units and first rows go out during the piece's last step.
-    constexpr int XU = kMpPiece * LU / kMpThreads;   // units of t_hi (and of t_lo) per thread per piece
+    constexpr int XU = PC * LU / kMpThreads;   // units of t_hi (and of t_lo) per thread per piece
     u32x4 hr[XU], lr[XU];
     auto t_load = [&](int p0) {
 #pragma unroll
@@ -1601,8 +1604,9 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2(const f16* __restrict__ p2, 
     };
     // p2 rows in the transposed pattern (256 contiguous bytes of a row per
     // 16 lanes), moved into the operand layout through this wave's LDS buffer
-    // (1-2 token blocks; more leave no LDS for the buffers)
-    constexpr bool TU = NB <= 2;
+    // (with 3-4 token blocks the pieces are 2 k-steps, so that the staged t
+    // leaves LDS for the buffers)
+    constexpr bool TU = NB >= 1;   // every token count (written so that it depends on NB)
     __shared__ u32x4 w_l[TU ? kMpThreads / kWave : 1][TU ? 16 * kTStride : 1];
     int rowt[1][4];
     bool rvt[1][4];
@@ -1639,20 +1643,20 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2(const f16* __restrict__ p2, 
       }
     };
     auto piece = [&](int p0, auto has_next) {
-      static_assert(kMpPiece == 4 || kMpPiece == 2, "the unrolled piece is 2 or 4 steps");
+      static_assert(PC == 4 || PC == 2, "the unrolled piece is 2 or 4 steps");
       rows(S1, p0 + 1);
-      if constexpr (kMpPiece == 4) {
+      if constexpr (PC == 4) {
         step(S0, 0);
         rows(S0, p0 + 2);
         step(S1, 1);
         rows(S1, p0 + 3);
       }
-      step(S0, kMpPiece - 2);
+      step(S0, PC - 2);
       if constexpr (decltype(has_next)::value) {
-        t_load(p0 + kMpPiece);
-        rows(S0, p0 + kMpPiece);
+        t_load(p0 + PC);
+        rows(S0, p0 + PC);
       }
-      step(S1, kMpPiece - 1);
+      step(S1, PC - 1);
       if constexpr (decltype(has_next)::value) {
         __syncthreads();                               // every wave is done with this piece's t
         t_store();
@@ -1683,7 +1687,7 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2(const f16* __restrict__ p2, 
       }
     };
     t_load(0);
-    if constexpr (TU) {
+    if constexpr (NB <= 2) {
       rows(D0[0], 0);
       rows(D0[1], 1);
     } else {
@@ -1692,16 +1696,16 @@ __global__ __launch_bounds__(kMpThreads) void k_mp2(const f16* __restrict__ p2, 
     t_store();
     __syncthreads();
     int p0 = 0;
-    if constexpr (TU) {
+    if constexpr (NB <= 2) {
       for (; p0 + kMpPiece < ns; p0 += kMpPiece) piece2(p0, std::true_type{});
       piece2(p0, std::false_type{});
     } else {
-      for (; p0 + kMpPiece < ns; p0 += kMpPiece) piece(p0, std::true_type{});
+      for (; p0 + PC < ns; p0 += PC) piece(p0, std::true_type{});
       piece(p0, std::false_type{});
     }
   }
-  for (int p0 = 0; p0 < ns && !whole; p0 += kMpPiece) {
-    const int np = ns - p0 < kMpPiece ? ns - p0 : kMpPiece;
+  for (int p0 = 0; p0 < ns && !whole; p0 += PC) {
+    const int np = ns - p0 < PC ? ns - p0 : PC;
     RowStep<f16, 1> cur;
     cur.load(p2, 0, row, rv, rank, p0 * kMuK, g);  // the first step's rows go out before the staging
     __syncthreads();                                // the previous piece is no longer read
