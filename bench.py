@@ -106,11 +106,36 @@ def kernel_source_sha256(names=None):
     return h.hexdigest()
 
 
+# Sources every kernel's behaviour depends on besides the file that defines
+# it: the host launch code (grids, chunking) and the shared device headers.
+KERNEL_COMMON_SOURCES = ["abi.hip", "pi_internal.h", "predict_device.h"]
+
+
+def kernel_defining_file(name):
+    """The csrc .hip file that defines the __global__ kernel `name`, or None."""
+    d = os.path.join(ROOT, "activation_sparse_rank_amd", "csrc")
+    pat = re.compile(r"__global__[^;{]*?\b" + re.escape(name) + r"\s*\(", re.S)
+    for f in sorted(os.listdir(d)):
+        if f.endswith(".hip"):
+            with open(os.path.join(d, f)) as fh:
+                if pat.search(fh.read()):
+                    return f
+    return None
+
+
+def kernel_sources(name):
+    """The csrc files kernel `name` is built from (defining file + common sources)."""
+    f = kernel_defining_file(name)
+    return None if f is None else sorted(set([f] + KERNEL_COMMON_SOURCES))
+
+
 def load_traffic(workload):
     """HBM bytes per dispatch of each kernel, from the committed rocprofv3 PMC
-    summary of this workload (profiles/*_traffic.md), or None when there is
-    none or the kernels have changed since it was taken (the summary names the
-    source files its kernels are built from)."""
+    summary of this workload (profiles/*_traffic.md).  Each kernel's entry
+    names the sources it was built from and their hash when the counters were
+    taken; a kernel whose sources have changed since is left out (its traffic
+    is then unknown), so one changed file never passes stale counts along.
+    None when there is no summary for the workload."""
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
         with open(path) as fh:
             m = re.search(r"```json\n(.*?)\n```", fh.read(), re.S)
@@ -119,10 +144,13 @@ def load_traffic(workload):
         data = json.loads(m.group(1))
         if data.get("workload") != workload:
             continue
-        if data.get("source_sha256") != kernel_source_sha256(data.get("source_files")):
-            return None
         fs, ws = data["fetch_scale"], data["write_scale"]
-        return {k: (v["fetch_kib"] * fs + v["write_kib"] * ws) * 1024.0 for k, v in data["kernels"].items()}
+        out = {}
+        for k, v in data["kernels"].items():
+            files = v.get("source_files")
+            if files and v.get("source_sha256") == kernel_source_sha256(files):
+                out[k] = (v["fetch_kib"] * fs + v["write_kib"] * ws) * 1024.0
+        return out
     return None
 
 

@@ -49,3 +49,54 @@ def test_down_rows_read_replace_listed_down_rows():
     assert bench.bytes_gather(cfg, 3277, 1, 3277) == bench.bytes_gather(cfg, 3277)
     ll = workload.get_config("llama70b")
     assert bench.bytes_active(ll, 2867, 1000) == (2 * 2867 + 1000) * rb
+
+
+def test_kernel_defining_file():
+    # the traffic summaries hash each kernel's own sources: the file that
+    # defines it is found by its __global__ declaration
+    assert bench.kernel_defining_file("k_mp2") == "k_mfma.hip"
+    assert bench.kernel_defining_file("k_down") == "k_gather.hip"
+    assert bench.kernel_defining_file("k_down_q4") == "k_gather.hip"
+    assert bench.kernel_defining_file("k_pred1") == "k_predict.hip"
+    assert bench.kernel_defining_file("k_compact_tiles") == "k_compact.hip"
+    assert bench.kernel_defining_file("k_no_such_kernel") is None
+    assert bench.kernel_sources("k_merge") == sorted({"k_gather.hip", *bench.KERNEL_COMMON_SOURCES})
+
+
+def test_traffic_counts_go_stale_per_kernel(tmp_path, monkeypatch):
+    # A tree with two kernels in two files: after one file changes, only the
+    # kernel it defines loses its counts.
+    import json
+    csrc = tmp_path / "activation_sparse_rank_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "include").mkdir()
+    (tmp_path / "include" / "pi.h").write_text("// header\n")
+    (csrc / "a.hip").write_text("__global__ void k_one(int* p) { *p = 1; }\n")
+    (csrc / "b.hip").write_text("__global__ __launch_bounds__(64) void k_two(int* p) { *p = 2; }\n")
+    for f in bench.KERNEL_COMMON_SOURCES:
+        (csrc / f).write_text("// common\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    kern = {}
+    for k in ("k_one", "k_two"):
+        src = bench.kernel_sources(k)
+        kern[k] = {"fetch_kib": 1.0, "write_kib": 1.0, "dispatches": 1, "source_files": src,
+                   "source_sha256": bench.kernel_source_sha256(src)}
+    data = {"workload": "w", "fetch_scale": 2.0, "write_scale": 1.0, "kernels": kern}
+    (tmp_path / "profiles" / "w_traffic.md").write_text("```json\n" + json.dumps(data) + "\n```\n")
+    assert set(bench.load_traffic("w")) == {"k_one", "k_two"}
+    assert bench.load_traffic("w")["k_one"] == 3.0 * 1024
+    (csrc / "b.hip").write_text("__global__ __launch_bounds__(64) void k_two(int* p) { *p = 3; }\n")
+    assert set(bench.load_traffic("w")) == {"k_one"}
+    (csrc / "abi.hip").write_text("// changed\n")        # a common source: every kernel
+    assert bench.load_traffic("w") == {}
+    assert bench.load_traffic("other") is None
+
+
+def test_committed_traffic_summaries_have_per_kernel_sources():
+    import glob, json, os, re
+    for path in glob.glob(os.path.join(bench.ROOT, "profiles", "*_traffic.md")):
+        data = json.loads(re.search(r"```json\n(.*?)\n```", open(path).read(), re.S).group(1))
+        assert data["kernels"], path
+        for k, v in data["kernels"].items():
+            assert v["source_files"] == bench.kernel_sources(k), (path, k)
