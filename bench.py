@@ -308,7 +308,13 @@ def _kernels(cfg, n_tok):
         if cfg.wtype == "f16" and n_tok <= 64 and ffn.startswith("k_xstep + "):
             ffn = ffn[len("k_xstep + "):]
         return f"{pred} (+ list) + {ffn}"
-    return f"{pred} + k_compact + {ffn}"
+    return f"{pred} + {_compact_kernel(cfg)} + {ffn}"
+
+
+def _compact_kernel(cfg):
+    """pi_compact's kernel: one workgroup per tile for 16-byte aligned mask
+    rows (the benchmark's masks are torch allocations, so aligned), else one."""
+    return "k_compact_tiles" if cfg.d_ff % 16 == 0 else "k_compact"
 
 
 def main(argv=None):
@@ -527,8 +533,8 @@ def main(argv=None):
     layer_roof = roof(f"pi_layer ({kern})", b_layer, ms_layer)
     parts = {
         "predict": roof(f"pi_predict ({_pred_kernels(cfg, B)})", b_pred, ms_pred),
-        "compact": {"kernel": "pi_compact (k_compact)", "avg_launch_us": round(ms_comp * 1e3, 3),
-                    "bytes_per_launch": int(b_comp)},
+        "compact": {"kernel": f"pi_compact ({_compact_kernel(cfg)})", "avg_launch_us": round(ms_comp * 1e3, 3),
+                    "bytes_per_launch": int(b_comp), "traffic": traffic_of(_compact_kernel(cfg))},
         "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, B)})", b_sp, ms_sp),
     }
     gather_read_gbps = round(b_listed / (ms_gr * 1e-3) / 1e9, 1)
