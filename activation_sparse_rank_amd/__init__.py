@@ -24,6 +24,7 @@ from .api import (  # noqa: F401
     predict,
     q4_0_repack,
     read_down_rows,
+    read_up_rows,
     read_flags,
     sparse_ffn,
     workspace_bytes,

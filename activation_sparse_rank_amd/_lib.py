@@ -21,7 +21,7 @@ STATUS_NAMES = {
 }
 
 # Every symbol include/pi.h declares.
-EXPORTS = ("pi_workspace_bytes", "pi_clear_flags", "pi_read_flags", "pi_read_down_rows", "pi_predict", "pi_compact",
+EXPORTS = ("pi_workspace_bytes", "pi_clear_flags", "pi_read_flags", "pi_read_down_rows", "pi_read_up_rows", "pi_predict", "pi_compact",
            "pi_sparse_ffn", "pi_layer", "pi_layer_noalloc", "pi_q4_0_repack", "pi_count_active", "pi_hot_order",
            "pi_rank_order", "pi_permute_rows", "pi_stream_read", "pi_gather_read", "pi_status_str", "pi_last_error")
 
@@ -32,6 +32,7 @@ PI_STREAM_BLOCKS = 2048  # entries of pi_stream_read's output (pi.h)
 PI_WS_HEADER_BYTES = 256
 PI_WS_FLAGS, PI_WS_WAIT_POLLS, PI_WS_SKIP_PUBLISH = 0, 1, 2
 PI_WS_DOWN_ROWS = 4   # 64-bit count of down-projection rows read, words 4 and 5
+PI_WS_UP_ROWS = 6     # 64-bit count of w_up rows read, words 6 and 7
 PI_FLAG_WAIT_EXPIRED, PI_FLAG_FP16_RANGE = 1, 2
 PI_NOALLOC_SCRATCH_BYTES = 32 << 20   # static scratch of pi_layer_noalloc (pi.h)
 
@@ -71,6 +72,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pi_read_flags.restype = ctypes.c_int
     lib.pi_read_down_rows.argtypes = [P, PP(ctypes.c_uint64), P]
     lib.pi_read_down_rows.restype = ctypes.c_int
+    lib.pi_read_up_rows.argtypes = [P, PP(ctypes.c_uint64), P]
+    lib.pi_read_up_rows.restype = ctypes.c_int
     lib.pi_predict.argtypes = [PP(PiPredictor), P, i32, i32, f32, P, P, P, sz, P]
     lib.pi_predict.restype = ctypes.c_int
     lib.pi_compact.argtypes = [P, i32, i32, P, P, P]

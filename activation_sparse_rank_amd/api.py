@@ -177,6 +177,15 @@ def read_down_rows(ws, stream=None) -> int:
     return int(out.value)
 
 
+def read_up_rows(ws, stream=None) -> int:
+    """How many w_up rows the up projections of the calls on ws have read,
+    summed over calls (pi_read_up_rows; synchronises that stream)."""
+    _dev(ws, "ws")
+    out = ctypes.c_uint64(0)
+    _check(L.load().pi_read_up_rows(ws.data_ptr(), ctypes.byref(out), _stream(stream)), "pi_read_up_rows")
+    return int(out.value)
+
+
 def _x(x, d, dtype, name="x"):
     _dev(x, name)
     if x.dtype != dtype:

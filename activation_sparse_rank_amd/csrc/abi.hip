@@ -162,6 +162,7 @@ pi::SparseArgs sparse_args(const pi_ffn* f, const void* x, int n_tok, const int3
   a.n_slices = L.n_slices;
   a.flags = reinterpret_cast<unsigned*>(ws);     // the header's flags word
   a.rows_read = reinterpret_cast<unsigned long long*>(reinterpret_cast<unsigned*>(ws) + PI_WS_DOWN_ROWS);
+  a.up_rows_read = reinterpret_cast<unsigned long long*>(reinterpret_cast<unsigned*>(ws) + PI_WS_UP_ROWS);
   a.fault = nullptr;
   return a;
 }
@@ -437,6 +438,17 @@ pi_status pi_read_down_rows(const void* ws, uint64_t* rows, void* stream) {
   if (!al16(ws)) return PI_E_ALIGN;
   const hipStream_t s = as_stream(stream);
   hipError_t e = hipMemcpyAsync(rows, static_cast<const unsigned*>(ws) + PI_WS_DOWN_ROWS, sizeof(uint64_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  return PI_OK;
+}
+
+pi_status pi_read_up_rows(const void* ws, uint64_t* rows, void* stream) {
+  if (!ws || !rows) return PI_E_NULL;
+  if (!al16(ws)) return PI_E_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = hipMemcpyAsync(rows, static_cast<const unsigned*>(ws) + PI_WS_UP_ROWS, sizeof(uint64_t),
                                 hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);

@@ -333,11 +333,13 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
   const unsigned long long am = __ballot(lane < kPURows && act_lds[lane < kPURows ? lane : 0] != 0);
 
   // ---- C: up projection of the active neurons: wave q computes part q of
-  // every active row, pu_batch rows at a time with all their loads in flight.
-  {
-    constexpr int S = ACT == ACT_REGLU ? pu_batch<WF>() / 2 : pu_batch<WF>();
-    unsigned long long bits = am;                  // the same in every wave
-    while (bits) {
+  // every listed row, pu_batch rows at a time with all their loads in flight.
+  // ReGLU: the gate rows first; a neuron whose gate is not positive for any
+  // token has h = 0 whatever its up row holds, so only the up rows of the
+  // neurons whose gate fires are read (fm).
+  auto rows_pass = [&](const void* w, unsigned long long bits, float (*dst)[kPURows][NT]) {
+    constexpr int S = pu_batch<WF>();
+    while (bits) {                                 // the same in every wave
       int rows[S], parts[S], rr[S];
       bool ok[S];
 #pragma unroll
@@ -349,34 +351,48 @@ __global__ __launch_bounds__(kPUThreads) void k_pred_up(const W* __restrict__ p2
         parts[s] = wave;
       }
       float pu[S][NT], pg[S][NT];
-      part_dots<WF, ACT == ACT_REGLU, NT, XL, S>(w_up, w_gate, scale_off, rows, parts, ok, d, xb, x_lds, nt, lane,
-                                                 pu, pg);
+      part_dots<WF, false, NT, XL, S>(w, w, scale_off, rows, parts, ok, d, xb, x_lds, nt, lane, pu, pg);
       if (lane == 0)
 #pragma unroll
         for (int s = 0; s < S; ++s)
           if (ok[s])
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-              pu_lds[wave][rr[s]][j] = pu[s][j];
-              if (ACT == ACT_REGLU) pg_lds[wave][rr[s]][j] = pg[s][j];
-            }
+            for (int j = 0; j < NT; ++j) dst[wave][rr[s]][j] = pu[s][j];
     }
+  };
+  unsigned long long fm = am;
+  if constexpr (ACT == ACT_REGLU) {
+    rows_pass(w_gate, am, pg_lds);
+    __syncthreads();                               // the gate part sums are in LDS
+    bool fire = false;
+    if (lane < kPURows && ((am >> lane) & 1ull)) {
+      const float b = bias ? bias[seg0 + lane] : 0.f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (j < nt)
+          fire |= (((pg_lds[0][lane][j] + pg_lds[1][lane][j]) + pg_lds[2][lane][j]) + pg_lds[3][lane][j]) + b > 0.f;
+    }
+    fm = __ballot(fire);                           // the same in every wave
   }
+  rows_pass(w_up, fm, pu_lds);
 
   // ---- D: the segment's slots ----
   __syncthreads();   // the part sums of phase C are in LDS
   if (wave == 0 && lane < kPURows && seg0 + lane < d_ff) {
     const int i = seg0 + lane;
-    const bool mine = (am >> lane) & 1ull;
-    act[i] = mine ? i : -1;
-    const float b = mine && bias ? bias[i] : 0.f;
+    const bool read = (fm >> lane) & 1ull;         // ReGLU: listed with a firing gate
+    // the slot names the neurons whose up row was read (ReGLU: a listed
+    // neuron whose gate fires for no token has h = 0 and is left out, which
+    // changes nothing downstream)
+    act[i] = read ? i : -1;
+    const float b = read && bias ? bias[i] : 0.f;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       if (j < nt) {
         const bool gt = ACT == ACT_REGLU;
         const float g0 = gt ? pg_lds[0][lane][j] : 0.f, g1 = gt ? pg_lds[1][lane][j] : 0.f;
         const float g2 = gt ? pg_lds[2][lane][j] : 0.f, g3 = gt ? pg_lds[3][lane][j] : 0.f;
-        h[(size_t)j * d_ff + i] = mine ? combine_parts<ACT>(pu_lds[0][lane][j], pu_lds[1][lane][j],
+        h[(size_t)j * d_ff + i] = read ? combine_parts<ACT>(pu_lds[0][lane][j], pu_lds[1][lane][j],
                                                             pu_lds[2][lane][j], pu_lds[3][lane][j], g0, g1, g2, g3, b)
                                        : 0.f;
       }
@@ -420,6 +436,8 @@ __device__ __forceinline__ bool any_nonzero(const float (&hv)[NT], int nt) {
 
 // Exclusive offset of this thread's c kept rows among the workgroup's, and
 // the workgroup's total: a wave scan, then the wave totals through LDS.
+// Callers pack a second count into the upper 16 bits of c (at most 2 per
+// thread, so neither half carries into the other); the scan adds both.
 __device__ __forceinline__ void kept_offsets(int c, int* wsum, int& pos, int& tot) {
   const int lane = lane_id(), wave = wave_id();
   int incl = c;
@@ -440,12 +458,14 @@ __device__ __forceinline__ void kept_offsets(int c, int* wsum, int& pos, int& to
 }
 
 // Slot form: the active neurons among [nb0, min(nb0 + kDnSlots, n1)) with a
-// nonzero h, in ascending order, into rows_l / h_l; returns how many.
+// nonzero h, in ascending order, into rows_l / h_l; returns how many, and
+// adds the number of valid slots (neurons whose up row was read) to *n_up.
 // Thread t takes neurons nb0 + 2t and nb0 + 2t + 1 (their act and h loads in
 // one round trip).
 template <int NT, int CAP>
 __device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, const float* __restrict__ h, int d_ff,
-                                           int nb0, int n1, int nt, int* rows_l, float (*h_l)[CAP], int* wsum) {
+                                           int nb0, int n1, int nt, int* rows_l, float (*h_l)[CAP], int* wsum,
+                                           int* n_up) {
   const int i0 = nb0 + 2 * (int)threadIdx.x, i1 = i0 + 1;
   const int a0 = i0 < n1 ? act[i0] : -1, a1 = i1 < n1 ? act[i1] : -1;
   float h0[NT], h1[NT];
@@ -454,10 +474,14 @@ __device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, cons
     h0[j] = j < nt && i0 < n1 ? h[(size_t)j * d_ff + i0] : 0.f;
     h1[j] = j < nt && i1 < n1 ? h[(size_t)j * d_ff + i1] : 0.f;
   }
-  const bool v0 = (unsigned)a0 < (unsigned)d_ff && any_nonzero<NT>(h0, nt);
-  const bool v1 = (unsigned)a1 < (unsigned)d_ff && any_nonzero<NT>(h1, nt);
+  const bool s0 = (unsigned)a0 < (unsigned)d_ff, s1 = (unsigned)a1 < (unsigned)d_ff;
+  const bool v0 = s0 && any_nonzero<NT>(h0, nt);
+  const bool v1 = s1 && any_nonzero<NT>(h1, nt);
   int pos, tot;
-  kept_offsets((v0 ? 1 : 0) + (v1 ? 1 : 0), wsum, pos, tot);
+  kept_offsets((v0 ? 1 : 0) + (v1 ? 1 : 0) + (((s0 ? 1 : 0) + (s1 ? 1 : 0)) << 16), wsum, pos, tot);
+  *n_up += tot >> 16;
+  pos &= 0xFFFF;
+  tot &= 0xFFFF;
   if (v0) {
     rows_l[pos] = a0;
 #pragma unroll
@@ -474,19 +498,25 @@ __device__ __forceinline__ int stage_slots(const int32_t* __restrict__ act, cons
 }
 
 // List form: the entries of list positions [pb, pb + n) (n <= kDnThreads)
-// that name a neuron and have a nonzero h, in list order; returns how many.
-// A malformed entry (outside [0, d_ff)) adds nothing.
+// that name a neuron and have a nonzero h, in list order; returns how many,
+// and adds the number of entries that name a neuron (the up rows the list
+// path reads) to *n_up.  A malformed entry (outside [0, d_ff)) adds nothing.
 template <int NT, int CAP>
 __device__ __forceinline__ int stage_list(const int32_t* __restrict__ idx, const float* __restrict__ h, int d_ff,
-                                          int pb, int n, int nt, int* rows_l, float (*h_l)[CAP], int* wsum) {
+                                          int pb, int n, int nt, int* rows_l, float (*h_l)[CAP], int* wsum,
+                                          int* n_up) {
   const int k = (int)threadIdx.x;
   const int i = k < n ? idx[pb + k] : -1;
   float hv[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) hv[j] = j < nt && k < n ? h[(size_t)j * d_ff + pb + k] : 0.f;
-  const bool v = (unsigned)i < (unsigned)d_ff && any_nonzero<NT>(hv, nt);
+  const bool named = (unsigned)i < (unsigned)d_ff;
+  const bool v = named && any_nonzero<NT>(hv, nt);
   int pos, tot;
-  kept_offsets(v ? 1 : 0, wsum, pos, tot);
+  kept_offsets((v ? 1 : 0) + ((named ? 1 : 0) << 16), wsum, pos, tot);
+  *n_up += tot >> 16;
+  pos &= 0xFFFF;
+  tot &= 0xFFFF;
   if (v) {
     rows_l[pos] = i;
 #pragma unroll
@@ -522,7 +552,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
                                                      const int32_t* __restrict__ count_ptr, int max_count,
                                                      const float* __restrict__ h, int nt, int n_chunks,
                                                      float* __restrict__ part,
-                                                     unsigned long long* __restrict__ rows_read) {
+                                                     unsigned long long* __restrict__ rows_read,
+                                                     unsigned long long* __restrict__ up_rows_read) {
   // SLOTS: idx is act[d_ff], h is [nt][d_ff] by neuron, count_ptr unused
   constexpr int E = 16 / sizeof(W);
   constexpr int SW = kWave * E;               // columns per slice
@@ -557,13 +588,14 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
     for (int e = 0; e < E; ++e) acc[j][e] = 0.f;
 
   const char* base = reinterpret_cast<const char*>(w_dt) + (size_t)col * sizeof(W);
-  int n_read = 0;
+  int n_read = 0, n_up = 0;
   for (int pb = k0; pb < k1; pb += CAP) {
     int n;
     if constexpr (SLOTS) {
-      n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum);
+      n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum, &n_up);
     } else {
-      n = stage_list<NT, CAP>(idx, h, d_ff, pb, k1 - pb < kDnPiece ? k1 - pb : kDnPiece, nt, rows_l, h_l, wsum);
+      n = stage_list<NT, CAP>(idx, h, d_ff, pb, k1 - pb < kDnPiece ? k1 - pb : kDnPiece, nt, rows_l, h_l, wsum,
+                              &n_up);
     }
     n_read += n;
     for (int jb = wave; jb < n; jb += kDnWaves * kDnUnroll) {
@@ -591,7 +623,10 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const W* __restrict__ w_dt,
   }
 
   // The column slices of a chunk read the same rows: slice 0 counts them.
-  if (rows_read && slice == 0 && threadIdx.x == 0 && n_read) atomicAdd(rows_read, (unsigned long long)n_read);
+  if (slice == 0 && threadIdx.x == 0) {
+    if (rows_read && n_read) atomicAdd(rows_read, (unsigned long long)n_read);
+    if (up_rows_read && n_up) atomicAdd(up_rows_read, (unsigned long long)n_up);
+  }
   // Sum the 8 waves in wave order, one token at a time; write the partials.
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -629,7 +664,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
                                                         const int32_t* __restrict__ count_ptr, int max_count,
                                                         const float* __restrict__ h, int nt, int n_chunks,
                                                         float* __restrict__ part,
-                                                        unsigned long long* __restrict__ rows_read) {
+                                                        unsigned long long* __restrict__ rows_read,
+                                                        unsigned long long* __restrict__ up_rows_read) {
   constexpr int CAP = SLOTS ? kDnSlots : kDnPiece;
   __shared__ float red[kDnWaves][kWave * 8];
   __shared__ int rows_l[CAP];
@@ -664,13 +700,14 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
 #pragma unroll
     for (int e = 0; e < kDqCols; ++e) acc[j][e] = 0.f;
 
-  int n_read = 0;
+  int n_read = 0, n_up = 0;
   for (int pb = k0; pb < k1; pb += CAP) {
     int n;
     if constexpr (SLOTS) {
-      n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum);
+      n = stage_slots<NT, CAP>(idx, h, d_ff, pb, k1, nt, rows_l, h_l, wsum, &n_up);
     } else {
-      n = stage_list<NT, CAP>(idx, h, d_ff, pb, k1 - pb < kDnPiece ? k1 - pb : kDnPiece, nt, rows_l, h_l, wsum);
+      n = stage_list<NT, CAP>(idx, h, d_ff, pb, k1 - pb < kDnPiece ? k1 - pb : kDnPiece, nt, rows_l, h_l, wsum,
+                              &n_up);
     }
     n_read += n;
     for (int jb = wave; jb < n; jb += kDnWaves * kDqUnroll) {
@@ -714,7 +751,10 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4(const uint8_t* __restric
     __syncthreads();
   }
 
-  if (rows_read && slice == 0 && threadIdx.x == 0 && n_read) atomicAdd(rows_read, (unsigned long long)n_read);
+  if (slice == 0 && threadIdx.x == 0) {
+    if (rows_read && n_read) atomicAdd(rows_read, (unsigned long long)n_read);
+    if (up_rows_read && n_up) atomicAdd(up_rows_read, (unsigned long long)n_up);
+  }
   // Sum the 8 waves in wave order, 8 columns per lane per round; write the partials.
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -805,10 +845,11 @@ hipError_t launch_down_form(const SparseArgs& a, int nt, hipStream_t s) {
   if constexpr (std::is_same<WF, Q4>::value)
     hipLaunchKernelGGL((k_down_q4<NT, SLOTS>), grid, dim3(kDnThreads), 0, s, static_cast<const uint8_t*>(a.w_down_t),
                        scale_offset<WF>(a), a.d, a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part,
-                       a.rows_read);
+                       a.rows_read, a.up_rows_read);
   else
     hipLaunchKernelGGL((k_down<WF, NT, SLOTS>), grid, dim3(kDnThreads), 0, s, static_cast<const WF*>(a.w_down_t), a.d,
-                       a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part, a.rows_read);
+                       a.d_ff, a.idx, a.count, a.max_count, a.h, nt, a.n_chunks, a.part, a.rows_read,
+                       a.up_rows_read);
   return hipGetLastError();
 }
 

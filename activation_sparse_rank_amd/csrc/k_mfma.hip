@@ -996,7 +996,8 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
                                                       const int32_t* __restrict__ count_ptr, int max_count,
                                                       const f16* __restrict__ h, int ldh, int nt, int n_chunks,
                                                       float* __restrict__ part,
-                                                      unsigned long long* __restrict__ rows_read) {
+                                                      unsigned long long* __restrict__ rows_read,
+                                                      unsigned long long* __restrict__ up_rows_read) {
   constexpr int NE = CPL * NB;             // accumulator quads per lane
   __shared__ float red[NE][4][kWave];
   const int lane = lane_id();
@@ -1010,9 +1011,10 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
   int tile = blockIdx.x, c = blockIdx.y;
   if constexpr (std::is_same<WF, Q4>::value) xcd_grouped(tile, c);
   const int kc0 = (int)((long long)c * ksteps / n_chunks), kc1 = (int)((long long)(c + 1) * ksteps / n_chunks);
-  if (rows_read && tile == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
+  if ((rows_read || up_rows_read) && tile == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
     const int r0 = kc0 * 32 < cnt ? kc0 * 32 : cnt, r1 = kc1 * 32 < cnt ? kc1 * 32 : cnt;
-    if (r1 > r0) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
+    if (r1 > r0 && rows_read) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
+    if (r1 > r0 && up_rows_read) atomicAdd(up_rows_read, (unsigned long long)(r1 - r0));   // k_mup read them too
   }
   const int kw0 = kc0 + wave * (kc1 - kc0) / kMdWaves, kw1 = kc0 + (wave + 1) * (kc1 - kc0) / kMdWaves;
   const int col = tile * 16 * CPL + n16 * CPL;
@@ -1318,7 +1320,8 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
                                                            const int32_t* __restrict__ count_ptr, int max_count,
                                                            const f16* __restrict__ h, int ldh, int nt, int n_chunks,
                                                            float* __restrict__ part,
-                                                           unsigned long long* __restrict__ rows_read) {
+                                                           unsigned long long* __restrict__ rows_read,
+                                                           unsigned long long* __restrict__ up_rows_read) {
   constexpr int HU = kMwPiece * 32 / 8;       // 16-byte units of one token's H in a piece
   constexpr int HS = HU + 1;                  // per-token stride in LDS: tokens on different banks
   __shared__ u32x4 h_l[16 * NB * HS];
@@ -1330,9 +1333,10 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_wide(const void* __restric
   const int ksteps = (cnt + 31) / 32;
   const int c = blockIdx.y;
   const int kc0 = (int)((long long)c * ksteps / n_chunks), kc1 = (int)((long long)(c + 1) * ksteps / n_chunks);
-  if (rows_read && blockIdx.x == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
+  if ((rows_read || up_rows_read) && blockIdx.x == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
     const int r0 = kc0 * 32 < cnt ? kc0 * 32 : cnt, r1 = kc1 * 32 < cnt ? kc1 * 32 : cnt;
-    if (r1 > r0) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
+    if (r1 > r0 && rows_read) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
+    if (r1 > r0 && up_rows_read) atomicAdd(up_rows_read, (unsigned long long)(r1 - r0));   // k_mup read them too
   }
   const int col = (blockIdx.x * kMdWaves + wave) * 16 * CPL + n16 * CPL;
   const bool cv = col < d;
@@ -1435,7 +1439,8 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
                                                          const int32_t* __restrict__ count_ptr, int max_count,
                                                          const f16* __restrict__ h, int ldh, int nt, int n_chunks,
                                                          float* __restrict__ part,
-                                                         unsigned long long* __restrict__ rows_read) {
+                                                         unsigned long long* __restrict__ rows_read,
+                                                         unsigned long long* __restrict__ up_rows_read) {
   constexpr int CPL = 4;
   constexpr int HU = kMwPiece * 32 / 8;       // 16-byte units of one token's H in a piece
   constexpr int HS = HU + 1;                  // per-token stride in LDS: tokens on different banks
@@ -1450,9 +1455,10 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
   int tile, c;
   xcd_grouped(tile, c);
   const int kc0 = (int)((long long)c * ksteps / n_chunks), kc1 = (int)((long long)(c + 1) * ksteps / n_chunks);
-  if (rows_read && tile == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
+  if ((rows_read || up_rows_read) && tile == 0 && threadIdx.x == 0) {     // the chunk's rows, counted once
     const int r0 = kc0 * 32 < cnt ? kc0 * 32 : cnt, r1 = kc1 * 32 < cnt ? kc1 * 32 : cnt;
-    if (r1 > r0) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
+    if (r1 > r0 && rows_read) atomicAdd(rows_read, (unsigned long long)(r1 - r0));
+    if (r1 > r0 && up_rows_read) atomicAdd(up_rows_read, (unsigned long long)(r1 - r0));   // k_mup read them too
   }
   const int col = (tile * kMdWaves + wave) * 16 * CPL + n16 * CPL;
   const bool cv = col < d;
@@ -1886,16 +1892,19 @@ hipError_t run_mtile(const SparseArgs& a, int t0, int nt, hipStream_t s) {
     const int tile = kMdWaves * 16 * 4;
     const dim3 grid((a.d + tile - 1) / tile, chunks);
     hipLaunchKernelGGL((k_mdown_w4<NB>), grid, dim3(kMdThreads), 0, s, static_cast<const f16*>(a.w_down_t), a.d,
-                       a.d_ff, a.idx, a.count, a.max_count, h, ldh, nt, chunks, a.part, a.rows_read);
+                       a.d_ff, a.idx, a.count, a.max_count, h, ldh, nt, chunks, a.part, a.rows_read,
+                       a.up_rows_read);
   } else if constexpr (NB >= wide_from<WF>()) {
     const int tile = kMdWaves * 16 * CPL;
     const dim3 grid((a.d + tile - 1) / tile, chunks);
     hipLaunchKernelGGL((k_mdown_wide<WF, NB, CPL>), grid, dim3(kMdThreads), 0, s, a.w_down_t, so, a.d, a.d_ff, a.idx,
-                       a.count, a.max_count, h, ldh, nt, chunks, a.part, a.rows_read);
+                       a.count, a.max_count, h, ldh, nt, chunks, a.part, a.rows_read,
+                       a.up_rows_read);
   } else {
     const dim3 grid((a.d + 16 * CPL - 1) / (16 * CPL), chunks);
     hipLaunchKernelGGL((k_mdown<WF, NB, CPL>), grid, dim3(kMdThreads), 0, s, a.w_down_t, so, a.d, a.d_ff, a.idx,
-                       a.count, a.max_count, h, ldh, nt, chunks, a.part, a.rows_read);
+                       a.count, a.max_count, h, ldh, nt, chunks, a.part, a.rows_read,
+                       a.up_rows_read);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -162,6 +162,8 @@ struct SparseArgs {
   const unsigned* fault = nullptr;
   // The header's 64-bit count of down-projection rows read; nullable.
   unsigned long long* rows_read = nullptr;
+  // The header's 64-bit count of w_up rows read; nullable.
+  unsigned long long* up_rows_read = nullptr;
 };
 hipError_t launch_sparse_ffn(const SparseArgs& a, hipStream_t s);
 

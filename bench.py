@@ -55,31 +55,36 @@ def bytes_compact(cfg, cnt, n_tok=1):
     return n_tok * cfg.d_ff + 4 * cnt + 4
 
 
-def bytes_active(cfg, cnt, down_rows=None):
-    """Bytes of the FFN weight rows a call needs: the up (and gate) rows of
-    the cnt listed neurons, and the down rows that are read -- every listed
-    row, or down_rows when given (the down projection leaves out rows whose
-    h is zero for every token, and counts the rows it reads)."""
+def bytes_active(cfg, cnt, down_rows=None, up_rows=None):
+    """Bytes of the FFN weight rows a call needs: the gate rows of the cnt
+    listed neurons (ReGLU), their up rows -- every listed row, or up_rows
+    when given (the fused ReGLU kernel leaves out the up rows of neurons
+    whose gate fires for no token, and counts the rows it reads) -- and the
+    down rows that are read: every listed row, or down_rows when given (the
+    down projection leaves out rows whose h is zero for every token, and
+    counts the rows it reads)."""
     down = cnt if down_rows is None else down_rows
-    return (cnt * (cfg.n_mat - 1) + down) * _row_bytes(cfg)
+    up = cnt if up_rows is None else up_rows
+    gate = cnt if cfg.n_mat == 3 else 0
+    return (gate + up + down) * _row_bytes(cfg)
 
 
-def bytes_gather(cfg, cnt, n_tok=1, down_rows=None):
+def bytes_gather(cfg, cnt, n_tok=1, down_rows=None, up_rows=None):
     """Algorithmic bytes of one pi_sparse_ffn call: the weight rows it needs
     (each read once for all tokens), the biases and list entries of the
     listed neurons, x and y."""
     xb = 2 if cfg.wtype == "q4_0" else ELEM_BYTES[cfg.wtype]
-    return bytes_active(cfg, cnt, down_rows) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model)
+    return bytes_active(cfg, cnt, down_rows, up_rows) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model)
 
 
-def bytes_layer(cfg, cnt, n_tok=1, down_rows=None):
+def bytes_layer(cfg, cnt, n_tok=1, down_rows=None, up_rows=None):
     """Algorithmic bytes of one pi_layer call: both predictor matrices and
     its bias, x, the FFN rows it needs (once for all tokens), the biases and
     list entries of the listed neurons, and y."""
     eb = ELEM_BYTES[cfg.pred_wtype]
     xb = 2 if cfg.wtype == "q4_0" else ELEM_BYTES[cfg.wtype]
     return ((cfg.rank * cfg.d_model + cfg.d_ff * cfg.rank) * eb + 4 * cfg.d_ff
-            + bytes_active(cfg, cnt, down_rows) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model))
+            + bytes_active(cfg, cnt, down_rows, up_rows) + 8 * cnt + n_tok * (cfg.d_model * xb + 4 * cfg.d_model))
 
 
 def flops_ffn(cfg, cnt, n_tok):
@@ -413,6 +418,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     # the timed steps, repeated: each repeat replays the same K steps
     rows_before = pi.read_down_rows(ws, stream)
+    up_before = pi.read_up_rows(ws, stream)
     rep_ms = []
     for r in range(max(1, args.repeats)):
         start = torch.cuda.Event(enable_timing=True)
@@ -433,6 +439,7 @@ def main(argv=None):
     flags_step = pi.read_flags(ws, stream)
     # down-projection rows the timed layer calls read (the workspace header's count)
     down_mean = (pi.read_down_rows(ws, stream) - rows_before) / (len(rep_ms) * args.steps * L)
+    up_mean = (pi.read_up_rows(ws, stream) - up_before) / (len(rep_ms) * args.steps * L)
     if flags_step:
         print(f"[bench] fault flags raised during the timed steps: {flags_step:#x}", file=sys.stderr, flush=True)
 
@@ -479,7 +486,7 @@ def main(argv=None):
             for k in mat_keys:
                 for view, rb in matrix_rows(cfg, layers[li], k):
                     pi.gather_read(view, idx[li], cnt[li:li + 1], row_bytes=rb, max_count=f, out=gr_out)
-    sp_rows0 = pi.read_down_rows(ws_s, stream)
+    sp_rows0, sp_up0 = pi.read_down_rows(ws_s, stream), pi.read_up_rows(ws_s, stream)
     # the dense-stream floor of the predictor: p1 and p2 of every layer read
     # with no arithmetic (pi_stream_read), each its own launch as in k_pred1 / k_pred2
     g_r1, g_r2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
@@ -498,12 +505,13 @@ def main(argv=None):
         ms_sp = _time_graph(g_sp, args.reps, stream) / L
         ms_gr = _time_graph(g_gr, args.reps, stream) / L
     sp_down = (pi.read_down_rows(ws_s, stream) - sp_rows0) / ((args.reps + 1) * L)
+    sp_up = (pi.read_up_rows(ws_s, stream) - sp_up0) / ((args.reps + 1) * L)
     last_cnt = cnt.cpu().numpy().astype(np.int64)
     last_mean = float(last_cnt.mean())
     b_pred = bytes_predict(cfg, B)
     b_comp = float(np.mean([bytes_compact(cfg, c, B) for c in last_cnt]))
-    b_sp = bytes_gather(cfg, last_mean, B, sp_down)
-    b_act = bytes_active(cfg, last_mean, sp_down)
+    b_sp = bytes_gather(cfg, last_mean, B, sp_down, sp_up)
+    b_act = bytes_active(cfg, last_mean, sp_down, sp_up)
     b_listed = bytes_active(cfg, last_mean)          # every listed row of every matrix
 
     traffic_table = load_traffic(f"{cfg.name} decode batch {B}")
@@ -526,8 +534,8 @@ def main(argv=None):
     stream_gbps = measure_stream(pi, dev, stream)
 
     # whole-layer bytes per layer call, averaged over the timed steps (bytes
-    # are linear in the list length and the down rows read)
-    b_layer = bytes_layer(cfg, cnt_mean, B, down_mean)
+    # are linear in the list length and the up and down rows read)
+    b_layer = bytes_layer(cfg, cnt_mean, B, down_mean, up_mean)
     ms_layer = ms_step / L
     kern = _kernels(cfg, B)
     layer_roof = roof(f"pi_layer ({kern})", b_layer, ms_layer)
@@ -586,6 +594,7 @@ def main(argv=None):
         "roofline_parts": parts,
         "count_mean": round(cnt_mean, 1),
         "down_rows_mean": round(down_mean, 1),
+        "up_rows_mean": round(up_mean, 1),
         "count_min": int(counts.min()),
         "count_max": int(counts.max()),
         "gen_seconds": round(t_gen, 1),
@@ -621,12 +630,13 @@ def main(argv=None):
             for li in range(L):
                 pi.sparse_ffn(ffns[li], x_pr[li], idx_m[li], cnt_m[li:li + 1], y_pr[li], ws=ws_ms)
         reps = max(2, args.reps // 4)
-        ml_rows0 = pi.read_down_rows(ws_m, stream)
+        ml_rows0, ml_up0 = pi.read_down_rows(ws_m, stream), pi.read_up_rows(ws_m, stream)
         with torch.cuda.stream(stream):
             ms_ml = _time_graph(g_ml, reps, stream) / L
             ms_mp = _time_graph(g_mp, reps, stream) / L
             ms_ms = _time_graph(g_ms, reps, stream) / L
         ml_down = (pi.read_down_rows(ws_m, stream) - ml_rows0) / ((reps + 1) * L)
+        ml_up = (pi.read_up_rows(ws_m, stream) - ml_up0) / ((reps + 1) * L)
         # the union's rows of every weight matrix read with no arithmetic
         g_mgr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_mgr, stream=stream):
@@ -638,7 +648,7 @@ def main(argv=None):
             ms_mgr = _time_graph(g_mgr, reps, stream) / L
         uc = cnt_m.cpu().numpy().astype(np.int64)
         uc_mean = float(uc.mean())
-        b_ml = bytes_layer(cfg, uc_mean, n, ml_down)
+        b_ml = bytes_layer(cfg, uc_mean, n, ml_down, ml_up)
         b_ms = bytes_gather(cfg, uc_mean, n)
         fl = float(np.mean([flops_ffn(cfg, c, n) for c in uc]))
         tflops = fl / (ms_ms * 1e-3) / 1e12
@@ -648,6 +658,7 @@ def main(argv=None):
             "n_tok": n,
             "union_count_mean": round(uc_mean, 1),
             "down_rows_mean": round(ml_down, 1),
+            "up_rows_mean": round(ml_up, 1),
             "layer_tokens_per_s": round(n / (ms_ml * 1e-3), 1),
             "layer": roof(f"pi_layer ({mk})", b_ml, ms_ml),
             "predict": roof(f"pi_predict ({_pred_kernels(cfg, n)})", bytes_predict(cfg, n), ms_mp),

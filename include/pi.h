@@ -133,6 +133,14 @@ size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n
  *     leaving it out changes no result (for finite weights).  The
  *     matrix-core down projection reads, and counts, every listed row once
  *     per token tile.
+ *   words PI_WS_UP_ROWS, PI_WS_UP_ROWS + 1: the same for the w_up rows the
+ *     up projections have read (pi_read_up_rows).  Every path reads the up
+ *     row of every listed neuron (the matrix cores once per token tile),
+ *     except pi_layer's fused kernel with ReGLU: it reads each listed
+ *     neuron's gate row first and its up row only when the gate is positive
+ *     for some token, since otherwise h = relu(gate) * up is zero whatever
+ *     the up row holds (again for finite weights).  A ReGLU call reads every
+ *     listed neuron's w_gate row.
  *
  * With one or two tokens pi_layer needs no list: the kernel that decides a
  * neuron writes a per-neuron slot (its index, or -1), and the down
@@ -150,6 +158,7 @@ size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n
 #define PI_WS_WAIT_POLLS 1
 #define PI_WS_SKIP_PUBLISH 2
 #define PI_WS_DOWN_ROWS 4
+#define PI_WS_UP_ROWS 6
 #define PI_FLAG_WAIT_EXPIRED 1u /* an in-kernel wait gave up; that call's y is all NaN            */
 #define PI_FLAG_FP16_RANGE 2u   /* a value the matrix-core path keeps in fp16 (the FFN's H, or the
                                    predictor's t) was not finite after rounding to fp16; the
@@ -161,7 +170,8 @@ size_t pi_workspace_bytes(const pi_predictor* pred, const pi_ffn* ffn, int32_t n
 pi_status pi_clear_flags(void* ws, void* stream);
 
 /* Read the flags word of ws into *flags (host memory).  One of the two
- * SYNCHRONOUS calls of this library (with pi_read_down_rows): it waits for
+ * SYNCHRONOUS calls of this library (with pi_read_down_rows and
+ * pi_read_up_rows): it waits for
  * the work queued on stream before it returns, so the flags of every earlier
  * call on that stream are included.
  * Errors: NULL pointers, ws not 16-byte aligned, PI_E_HIP.  */
@@ -171,6 +181,10 @@ pi_status pi_read_flags(const void* ws, uint32_t* flags, void* stream);
  * into *rows (host memory).  SYNCHRONOUS, like pi_read_flags.
  * Errors: NULL pointers, ws not 16-byte aligned, PI_E_HIP.  */
 pi_status pi_read_down_rows(const void* ws, uint64_t* rows, void* stream);
+
+/* The same for the count of w_up rows read (PI_WS_UP_ROWS).  SYNCHRONOUS.
+ * Errors: NULL pointers, ws not 16-byte aligned, PI_E_HIP.  */
+pi_status pi_read_up_rows(const void* ws, uint64_t* rows, void* stream);
 
 /* Predict which neurons each token activates.
  *   x:      [n_tok][d_model], dtype xtype == pred->wtype

@@ -191,6 +191,9 @@ def test_flag_calls_reject(lib):
     assert lib.pi_read_down_rows(None, ctypes.byref(rows), None) == L.PI_E_NULL
     assert lib.pi_read_down_rows(FAKE, None, None) == L.PI_E_NULL
     assert lib.pi_read_down_rows(FAKE_ODD, ctypes.byref(rows), None) == L.PI_E_ALIGN
+    assert lib.pi_read_up_rows(None, ctypes.byref(rows), None) == L.PI_E_NULL
+    assert lib.pi_read_up_rows(FAKE, None, None) == L.PI_E_NULL
+    assert lib.pi_read_up_rows(FAKE_ODD, ctypes.byref(rows), None) == L.PI_E_ALIGN
 
 
 def test_workspace_has_header(lib):

@@ -51,6 +51,20 @@ def test_down_rows_read_replace_listed_down_rows():
     assert bench.bytes_active(ll, 2867, 1000) == (2 * 2867 + 1000) * rb
 
 
+def test_up_rows_read_replace_listed_up_rows():
+    # The fused ReGLU kernel reads a listed neuron's up row only when its gate
+    # fires for some token and counts the up rows it reads; the gate rows of
+    # every listed neuron are still read.
+    ll = workload.get_config("llama70b")
+    rb = 8192 * 2
+    assert bench.bytes_active(ll, 2867, 1000, 1200) == (2867 + 1200 + 1000) * rb
+    assert bench.bytes_active(ll, 2867, None, 2867) == bench.bytes_active(ll, 2867)
+    assert bench.bytes_layer(ll, 2867, 1, 1000, 1200) == bench.bytes_layer(ll, 2867, 1, 1000) - (2867 - 1200) * rb
+    assert bench.bytes_gather(ll, 2867, 1, None, 0) == bench.bytes_gather(ll, 2867) - 2867 * rb
+    fc = workload.get_config("falcon40b")     # ReLU: no gate matrix
+    assert bench.bytes_active(fc, 3277, 1456, 3000) == (3000 + 1456) * rb
+
+
 def test_kernel_defining_file():
     # the traffic summaries hash each kernel's own sources: the file that
     # defines it is found by its __global__ declaration

@@ -1,13 +1,16 @@
-"""GPU: the workspace header's count of down-projection rows read.
+"""GPU: the workspace header's counts of w_down and w_up rows read.
 
 The list-path down projection (up to one token tile of 8; Q4_0: the tile
 whose fp16 x fits 32 KB) reads only the listed rows whose h is nonzero for
 some token of the tile, since a row whose h is exactly zero for every token
 adds nothing to y.  The matrix-core path reads every listed row once per
-token tile.  The expected counts are built from the oracle's dense FFN (its
-firing flags: a ReLU / squared-ReLU neuron fires when its pre-activation is
-positive, a ReGLU neuron when its gate is), and the list from pi_compact,
-which the parity tests hold bit-exact to the oracle.
+token tile.  The up projections read the up row of every listed neuron once
+per token tile, except pi_layer's fused kernel with ReGLU, which reads the
+up row only of the listed neurons whose gate is positive for some token.
+The expected counts are built from the oracle's dense FFN (its firing flags:
+a ReLU / squared-ReLU neuron fires when its pre-activation is positive, a
+ReGLU neuron when its gate is), and the list from pi_compact, which the
+parity tests hold bit-exact to the oracle.
 """
 
 import numpy as np
@@ -54,6 +57,21 @@ def _expected(fired, idx, n_tok, wtype):
     return total
 
 
+def _tiles(wtype, n_tok):
+    t = MFMA_TILE if _mfma(wtype, n_tok) else LIST_TILE
+    return (n_tok + t - 1) // t
+
+
+def _expected_up(fired, idx, n_tok, wtype, act, layer):
+    """w_up rows the up projections read: every listed row once per token
+    tile, or, in pi_layer's fused kernel (one tile, no matrix cores) with
+    ReGLU, the listed rows whose gate fires for some token."""
+    fused = layer and n_tok <= LIST_TILE and not _mfma(wtype, n_tok)
+    if fused and act == "reglu":
+        return int(fired[:n_tok][:, idx].any(axis=0).sum())
+    return len(idx) * _tiles(wtype, n_tok)
+
+
 @pytest.mark.parametrize("wtype", ["f32", "f16", "q4_0"])
 @pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
 @pytest.mark.parametrize("n_tok", [1, 2, 9])
@@ -77,20 +95,29 @@ def test_rows_read(wtype, act, n_tok):
 
     y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
     ws = pi.alloc_workspace(None, dl.ffn, n_tok)
-    assert pi.read_down_rows(ws) == 0
+    assert pi.read_down_rows(ws) == 0 and pi.read_up_rows(ws) == 0
     pi.sparse_ffn(dl.ffn, x, idx, cnt, y, ws=ws)
     got = pi.read_down_rows(ws)
     assert abs(got - want) <= SLACK, f"{what}: pi_sparse_ffn read {got} rows, expected {want}"
+    up = pi.read_up_rows(ws)
+    want_up = _expected_up(fired, listed, n_tok, wtype, act, layer=False)
+    assert up == want_up, f"{what}: pi_sparse_ffn read {up} up rows, expected {want_up}"
     pi.sparse_ffn(dl.ffn, x, idx, cnt, y, ws=ws)
     assert pi.read_down_rows(ws) == 2 * got, f"{what}: the count does not add up over calls"
+    assert pi.read_up_rows(ws) == 2 * up, f"{what}: the up count does not add up over calls"
     pi.clear_flags(ws)
-    assert pi.read_down_rows(ws) == 0
+    assert pi.read_down_rows(ws) == 0 and pi.read_up_rows(ws) == 0
 
     # the layer call lists the same neurons (fused path: by slots)
     wl = pi.alloc_workspace(dl.pred, dl.ffn, n_tok)
     pi.layer(dl.pred, dl.ffn, x, cfg.tau, y, ws=wl)
     got_l = pi.read_down_rows(wl)
     assert abs(got_l - want) <= SLACK, f"{what}: pi_layer read {got_l} rows, expected {want}"
+    up_l = pi.read_up_rows(wl)
+    want_up = _expected_up(fired, listed, n_tok, wtype, act, layer=True)
+    assert abs(up_l - want_up) <= SLACK, f"{what}: pi_layer read {up_l} up rows, expected {want_up}"
+    if act == "reglu" and n_tok <= 2:
+        assert want_up < c, f"{what}: the case should have listed neurons whose gate does not fire"
     assert pi.read_flags(wl) == 0
 
 
@@ -109,4 +136,23 @@ def test_all_zero_h_reads_nothing():
     ws = pi.alloc_workspace(None, dl.ffn, 1)
     pi.sparse_ffn(dl.ffn, x, idx, cnt, y, ws=ws)
     assert pi.read_down_rows(ws) == 0
+    assert pi.read_up_rows(ws) == f      # every listed up row is read; none passes h != 0
+    assert torch.all(y == 0)
+
+
+def test_reglu_gate_never_fires_reads_no_up_row():
+    # pi_layer's fused kernel with ReGLU and a gate bias of -1e4: every gate is
+    # negative, so no up row and no down row is read and y is exactly zero.
+    cfg = _cfg("f16", "reglu")
+    dl = DeviceLayer(cfg)
+    f, d = cfg.d_ff, cfg.d_model
+    dl.ffn = pi.FFN(dl.L["w_up"], dl.L["w_down_t"], "reglu", w_gate=dl.L["w_gate"],
+                    b_gate=torch.full((f,), -1e4, dtype=torch.float32, device="cuda"))
+    x = workload.make_tokens(cfg, 0, 1, "cuda")
+    y = torch.full((1, d), float("nan"), dtype=torch.float32, device="cuda")
+    ws = pi.alloc_workspace(dl.pred, dl.ffn, 1)
+    pi.layer(dl.pred, dl.ffn, x, 0.5, y, ws=ws)
+    assert pi.read_up_rows(ws) == 0
+    assert pi.read_down_rows(ws) == 0
+    assert pi.read_flags(ws) == 0
     assert torch.all(y == 0)
