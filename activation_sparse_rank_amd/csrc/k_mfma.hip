@@ -306,6 +306,30 @@ __device__ __forceinline__ void rows_for_load(const int (&row)[MB], const bool (
 // are one contiguous block, so the many workgroups reading them at once
 // spread over the L2 channels instead of meeting on the few that a 16 KB row
 // stride maps to.
+// Q4_0 code groups of 16 rows x 4 k-steps (256 contiguous bytes of each
+// row), loaded 16 lanes per row, 4 rows per instruction (lane l: row 4i +
+// l/16, 16-byte unit l%16), and moved into the operand layout through the
+// wave's LDS buffer: steps() gives lane l, for step s of the window, the
+// code group of row l%16 and lane group l/16 (the group that
+// RowStep<Q4>::load_codes gives that lane for that step).
+struct CodesTU {
+  u32x4 v[4];
+  __device__ __forceinline__ void load(const uint8_t* codes, const int (&rowt)[4], size_t row_bytes, size_t off,
+                                       int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ld_nt(codes + (size_t)rowt[i] * row_bytes + off + 16 * (lane & 15));
+  }
+  __device__ __forceinline__ void steps(u32x4* buf, int lane, u32x4 (&c)[4]) const {
+    const int q = lane >> 4, u = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[(4 * i + q) * kTStride + u] = v[i];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // the writes land before any lane reads
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c[s] = buf[u * kTStride + 4 * s + q];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // and the reads before the next window's writes
+  }
+};
+
 template <int NB>
 struct TokStep {
   u32x4 v[NB][4];
@@ -428,9 +452,10 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   constexpr int QT = quads_per_thread<NQ>();
   constexpr bool TR = std::is_same<WF, f16>::value && !GATED;   // transposed row loads (RowStepT)
   __shared__ float red[kMuWaves][NQ][4][kWave];
-  __shared__ u32x4 w_l[TR ? kMuWaves : 1][TR ? 16 * kTStride : 1];
   constexpr bool Q = std::is_same<WF, Q4>::value;
-  __shared__ u32x4 sc_l[Q ? kMuWaves : 1][Q ? MB : 1][16][Q ? 4 : 1];   // Q4_0: a chunk's scales per row
+  constexpr bool TQ = Q && MB == 1;   // Q4_0 code groups by transposed loads (CodesTU)
+  __shared__ u32x4 w_l[TR || TQ ? kMuWaves : 1][TR || TQ ? 16 * kTStride : 1];
+  __shared__ u32x4 sc_l[Q ? kMuWaves : 1][Q && GATED ? 2 : 1][Q ? MB : 1][16][Q ? 4 : 1];   // Q4_0: a chunk's scales
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -461,8 +486,8 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   const int s0 = wave * ns / kMuWaves, s1 = (wave + 1) * ns / kMuWaves;
   int rowt[MB][4];
   bool rvt[MB][4];
-  if constexpr (TR) rows_for_load<MB>(row, rv, lane, rowt, rvt);
-  u32x4* wbuf = &w_l[TR ? wave : 0][0];
+  if constexpr (TR || TQ) rows_for_load<MB>(row, rv, lane, rowt, rvt);
+  u32x4* wbuf = &w_l[TR || TQ ? wave : 0][0];
   // fp16 rows: every lane loads (stand-in rows and token slots; see RowStepTU)
   using Rows = typename std::conditional<TR, RowStepTU<MB>, RowStep<WF, MB>>::type;
   using Toks = typename std::conditional<TR, TokStepClamped<NB>, TokStep<NB>>::type;
@@ -510,39 +535,74 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
     bool all[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) all[mb] = true;
-    // The up rows' scales of a whole chunk (4 per step, 8 bytes per step and
-    // row, contiguous) in one 16-byte load per lane -- lane (g, n16) takes
-    // unit g % SU of row n16 -- staged in this wave's LDS: a 2-byte load per
-    // lane and step otherwise costs as many memory instructions as the codes.
-    // Needs 16-byte aligned scale rows (d % 256 == 0) and whole chunks.
+    // The rows' scales of a whole chunk (4 per step, 8 bytes per step and
+    // row, contiguous) in one 16-byte load per lane and matrix -- lane (g,
+    // n16) takes unit g % SU of row n16 -- staged in this wave's LDS: a 2-byte
+    // load per lane and step otherwise costs as many memory instructions as
+    // the codes.  With one row block the code groups come by transposed loads
+    // (CodesTU).  Needs 16-byte aligned scale rows (d % 256 == 0) and whole
+    // chunks.
     constexpr int SU = kQPre / 2;                   // 16-byte scale units per row per chunk
+    constexpr int NM = GATED ? 2 : 1;               // matrices: up (and gate)
     const int nbk = d / 32;
-    const bool sc_chunk = !GATED && nbk % 8 == 0 && (s1 - s0) % kQPre == 0;
-    const uint8_t* sc_base = static_cast<const uint8_t*>(w_up) + scale_off;
+    const bool sc_chunk = nbk % 8 == 0 && (s1 - s0) % kQPre == 0;
+    const uint8_t* wm[2] = {static_cast<const uint8_t*>(w_up),
+                            static_cast<const uint8_t*>(GATED ? w_gate : w_up)};
     for (int c0 = s0; c0 < s1; c0 += kQPre) {
       RowStep<WF, MB> up[kQPre];
       RowStep<WF, GATED ? MB : 1> gt[GATED ? kQPre : 1];
       bool chunked = false;
-      if constexpr (!GATED) {
-        if (sc_chunk) {
-          u32x4 su[MB];
+      if (sc_chunk) {
+        u32x4 su[NM][MB];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            su[mb] = ld_nt(sc_base + ((size_t)row[mb] * nbk + (size_t)c0 * 4) * 2 + 16 * (g % SU));
+            su[m][mb] = ld_nt(wm[m] + scale_off + ((size_t)row[mb] * nbk + (size_t)c0 * 4) * 2 + 16 * (g % SU));
+        CodesTU ct[TQ ? NM : 1][2];
+        if constexpr (TQ) {
+          static_assert(kQPre == 8, "two 4-step windows per chunk");
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              ct[m][h].load(wm[m], rowt[0], (size_t)nbk * 16, ((size_t)c0 * 4 + 16 * h) * 16, lane);
+        } else {
 #pragma unroll
           for (int j = 0; j < kQPre; ++j) up[j].load_codes(w_up, row, d, (c0 + j) * kMuK, g);
+          if constexpr (GATED)
+#pragma unroll
+            for (int j = 0; j < kQPre; ++j) gt[j].load_codes(w_gate, row, d, (c0 + j) * kMuK, g);
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            if (g < SU) sc_l[wave][mb][n16][g] = su[mb];
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // the scales land before any lane reads
+            if (g < SU) sc_l[wave][m][mb][n16][g] = su[m][mb];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // the scales land before any lane reads
 #pragma unroll
-          for (int j = 0; j < kQPre; ++j)
+        for (int j = 0; j < kQPre; ++j)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              up[j].sc[mb] = reinterpret_cast<const f16*>(&sc_l[wave][mb][n16][0])[4 * j + g];
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // and are read before the next chunk's writes
-          chunked = true;
+          for (int mb = 0; mb < MB; ++mb) {
+            up[j].sc[mb] = reinterpret_cast<const f16*>(&sc_l[wave][0][mb][n16][0])[4 * j + g];
+            if constexpr (GATED) gt[j].sc[mb] = reinterpret_cast<const f16*>(&sc_l[wave][NM - 1][mb][n16][0])[4 * j + g];
+          }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // and are read before the next chunk's writes
+        if constexpr (TQ) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x4 c[4];
+            ct[0][h].steps(wbuf, lane, c);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) up[4 * h + s2].code[0] = c[s2];
+            if constexpr (GATED) {
+              ct[NM - 1][h].steps(wbuf, lane, c);
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) gt[4 * h + s2].code[0] = c[s2];
+            }
+          }
         }
+        chunked = true;
       }
       if (!chunked) {
 #pragma unroll
