@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
   // sets, the next one loading while the current one is multiplied.
   constexpr bool kPipe = !(GATED && NB > 2) && !std::is_same<WF, Q4>::value;
   if constexpr (std::is_same<WF, Q4>::value) {
-    constexpr int kQPre = 8 / MB;
+    constexpr int kQPre = GATED && MB == 1 ? 4 : 8 / MB;   // k steps per chunk
     bool all[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) all[mb] = true;
@@ -559,13 +559,14 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             su[m][mb] = ld_nt(wm[m] + scale_off + ((size_t)row[mb] * nbk + (size_t)c0 * 4) * 2 + 16 * (g % SU));
-        CodesTU ct[TQ ? NM : 1][2];
+        constexpr int NWIN = kQPre / 4 > 0 ? kQPre / 4 : 1;
+        CodesTU ct[TQ ? NM : 1][NWIN];
         if constexpr (TQ) {
-          static_assert(kQPre == 8, "two 4-step windows per chunk");
+          static_assert(kQPre % 4 == 0, "whole 4-step windows per chunk");
 #pragma unroll
           for (int m = 0; m < NM; ++m)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < NWIN; ++h)
               ct[m][h].load(wm[m], rowt[0], (size_t)nbk * 16, ((size_t)c0 * 4 + 16 * h) * 16, lane);
         } else {
 #pragma unroll
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(kMuThreads) void k_mup(const void* __restrict__ w_u
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");     // and are read before the next chunk's writes
         if constexpr (TQ) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+          for (int h = 0; h < NWIN; ++h) {
             u32x4 c[4];
             ct[0][h].steps(wbuf, lane, c);
 #pragma unroll
