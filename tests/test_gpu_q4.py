@@ -132,6 +132,34 @@ def test_sparse_ffn_q4_mfma(d, f, act, n_tok):
         check_y(host(y), ref, TOL["q4_0"], f"q4 mfma {act} d={d} f={f} n={n_tok} density={density}")
 
 
+@pytest.mark.parametrize("d", [1152, 2048, 4096])
+@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("n_tok", [9, 16])
+def test_q4_mup_chunking(d, act, n_tok):
+    # The matrix-core up projection at up to 16 tokens walks each wave's
+    # quarter of d in chunks of k steps (8, or 4 with gate rows), with the
+    # chunk's scales in one load and the code groups by transposed loads;
+    # quarters that are not whole chunks, or rows whose scales are not
+    # 16-byte aligned (d % 256 != 0), take the step-by-step loads instead.
+    # d = 1152: 9 steps, ragged quarters, unaligned scales; 2048: quarters of
+    # 4 steps (one gated chunk, step-by-step without gate); 4096: quarters of
+    # 8 steps (one chunk, or two gated chunks).
+    f = 600
+    ffn, hk, _ = _q4_ffn(d, f, act, seed=3 * d + n_tok)
+    g = torch.Generator(device="cuda").manual_seed(d + n_tok)
+    x = torch.randn((n_tok, d), generator=g, device="cuda").to(torch.float16)
+    sel = torch.rand(f, generator=g, device="cuda") < 0.3
+    idx_list = torch.nonzero(sel).flatten().to(torch.int32)
+    n = idx_list.numel()
+    idx = _i32(f)
+    idx[:n] = idx_list
+    cnt = torch.tensor([n], dtype=torch.int32, device="cuda")
+    y = torch.empty((n_tok, d), dtype=torch.float32, device="cuda")
+    pi.sparse_ffn(ffn, x, idx, cnt, y)
+    ref = oracle.sparse_ffn(host(x), host(idx_list), **hk)
+    check_y(host(y), ref, TOL["q4_0"], f"q4 mup chunking {act} d={d} n={n_tok}")
+
+
 def test_q4_empty_and_all():
     d, f, n_tok = 1024, 512, 3
     ffn, hk, _ = _q4_ffn(d, f, "reglu", seed=11)
