@@ -516,17 +516,17 @@ def main(argv=None):
 
     traffic_table = load_traffic(f"{cfg.name} decode batch {B}")
 
-    def traffic_of(kernels):
+    def traffic_of(kernels, table=traffic_table):
         # measured HBM bytes per call of the kernel set named in the label
         names = re.findall(r"k_[a-z0-9_]+", kernels)
-        if traffic_table is None or not names or any(k not in traffic_table for k in names):
+        if table is None or not names or any(k not in table for k in names):
             return None
-        return int(sum(traffic_table[k] for k in names))
+        return int(sum(table[k] for k in names))
 
-    def roof(kernels, b, ms):
+    def roof(kernels, b, ms, table=traffic_table):
         gbps = b / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "kernel": kernels, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_of(kernels),
+                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_of(kernels, table),
                 "bytes_per_launch": int(b), "avg_launch_us": round(ms * 1e3, 3)}
 
     # achievable HBM read bandwidth: a plain streaming read (pi_stream_read)
@@ -653,6 +653,7 @@ def main(argv=None):
         fl = float(np.mean([flops_ffn(cfg, c, n) for c in uc]))
         tflops = fl / (ms_ms * 1e-3) / 1e12
         mk = _kernels(cfg, n)
+        traffic_pr = load_traffic(f"{cfg.name} prompt {n}")
         out["multi_token"] = {
             "what": f"one prompt of {n} tokens per layer, per-token masks OR-ed into one list",
             "n_tok": n,
@@ -660,9 +661,9 @@ def main(argv=None):
             "down_rows_mean": round(ml_down, 1),
             "up_rows_mean": round(ml_up, 1),
             "layer_tokens_per_s": round(n / (ms_ml * 1e-3), 1),
-            "layer": roof(f"pi_layer ({mk})", b_ml, ms_ml),
-            "predict": roof(f"pi_predict ({_pred_kernels(cfg, n)})", bytes_predict(cfg, n), ms_mp),
-            "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, n)})", b_ms, ms_ms),
+            "layer": roof(f"pi_layer ({mk})", b_ml, ms_ml, traffic_pr),
+            "predict": roof(f"pi_predict ({_pred_kernels(cfg, n)})", bytes_predict(cfg, n), ms_mp, traffic_pr),
+            "gather": roof(f"pi_sparse_ffn ({_ffn_kernels(cfg, n)})", b_ms, ms_ms, traffic_pr),
             "gather_mfma": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                             "frac": round(tflops / 2500.0, 4), "flops_per_launch": fl},
             "gather_read": {"what": "pi_gather_read of the union's rows of every weight matrix, no arithmetic",
