@@ -400,6 +400,28 @@ __device__ __forceinline__ void pipeline2(int s0, int s1, Stage& A, Stage& B, Lo
   }
 }
 
+// Three register stages over a number of steps that is a multiple of 3
+// (at least 3): the loads of steps st+1 and st+2 are in flight while step st
+// is multiplied, and no load's issue depends on a branch.
+template <typename Stage, typename Load, typename Mul>
+__device__ __forceinline__ void pipeline3x(int s0, int s1, Stage& A, Stage& B, Stage& C, Load load, Mul mul) {
+  load(A, s0);
+  load(B, s0 + 1);
+  int st = s0;
+  for (; st + 3 < s1; st += 3) {
+    load(C, st + 2);
+    mul(A);
+    load(A, st + 3);
+    mul(B);
+    load(B, st + 4);
+    mul(C);
+  }
+  load(C, st + 2);
+  mul(A);
+  mul(B);
+  mul(C);
+}
+
 // k_xstep: xs[st][t][128] = x[t][128 st .. 128 st + 128), the step-major copy
 // TokStep reads.  With BLOCK (operands meeting Q4_0 rows, which come in block
 // order) the 16-byte groups inside a step are also permuted:
@@ -1494,8 +1516,10 @@ __device__ __forceinline__ void transpose8x4(const u32x2 (&in)[8], u32x4 (&out)[
 // operands are formed), and with 256 columns per workgroup 16 list chunks
 // still give 512 workgroups at the Falcon width, so the partial sums that
 // the merge reads back are half as many bytes as with 32 chunks.
+constexpr int kW4Piece = 18;                 // k-steps per staged piece: a multiple of the 3 row stages
+
 template <int NB>
-__global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__ w_dt, int d, int d_ff,
+__global__ __launch_bounds__(kMdThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_mdown_w4(const f16* __restrict__ w_dt, int d, int d_ff,
                                                          const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ count_ptr, int max_count,
                                                          const f16* __restrict__ h, int ldh, int nt, int n_chunks,
@@ -1503,10 +1527,10 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
                                                          unsigned long long* __restrict__ rows_read,
                                                          unsigned long long* __restrict__ up_rows_read) {
   constexpr int CPL = 4;
-  constexpr int HU = kMwPiece * 32 / 8;       // 16-byte units of one token's H in a piece
+  constexpr int HU = kW4Piece * 32 / 8;       // 16-byte units of one token's H in a piece
   constexpr int HS = HU + 1;                  // per-token stride in LDS: tokens on different banks
   __shared__ u32x4 h_l[16 * NB * HS];
-  __shared__ int rows_l[kMwPiece * 32];
+  __shared__ int rows_l[kW4Piece * 32];
   const int lane = lane_id();
   const int wave = wave_id();
   const int g = lane >> 4, n16 = lane & 15;
@@ -1561,8 +1585,8 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
       for (int nb = 0; nb < NB; ++nb) acc[j][nb] = mfma(a[nb], bt[j], acc[j][nb]);
   };
 
-  for (int pb = kc0; pb < kc1; pb += kMwPiece) {
-    const int np = kc1 - pb < kMwPiece ? kc1 - pb : kMwPiece;
+  for (int pb = kc0; pb < kc1; pb += kW4Piece) {
+    const int np = kc1 - pb < kW4Piece ? kc1 - pb : kW4Piece;
     __syncthreads();                           // the previous piece is no longer read
     for (int e = threadIdx.x; e < np * 32; e += kMdThreads) {
       const int p = pb * 32 + e;
@@ -1575,8 +1599,11 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown_w4(const f16* __restrict__
       h_l[t * HS + u] = p < cnt ? ld16(h + (size_t)t * ldh + p) : u32x4{0, 0, 0, 0};
     }
     __syncthreads();
-    Stage S0, S1;
-    pipeline2(0, np, S0, S1, load_rows, mul_rows);
+    Stage S0, S1, S2;
+    if (np == kW4Piece)
+      pipeline3x(0, np, S0, S1, S2, load_rows, mul_rows);
+    else
+      pipeline2(0, np, S0, S1, load_rows, mul_rows);
   }
 
   if (cv) {
