@@ -1026,6 +1026,20 @@ struct DownRows<f16, CPL> {
 #pragma unroll
     for (int r = 0; r < 8; ++r) out[r] = v[r][q];
   }
+  // Every lane loads (the caller passes a valid stand-in row and column for
+  // entries it does not use); group_ok then zeroes the rows with ok false.
+  __device__ __forceinline__ void load_all(const void* w, size_t, int d, const int (&rows)[8], int col) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const char* p = static_cast<const char*>(w) + ((size_t)rows[r] * d + col) * sizeof(f16);
+#pragma unroll
+      for (int q = 0; q < CPL / 8; ++q) v[r][q] = ld_nt(p + 16 * q);
+    }
+  }
+  __device__ __forceinline__ void group_ok(int q, const bool (&ok)[8], u32x4 (&out)[8]) const {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) out[r] = ok[r] ? v[r][q] : u32x4{0, 0, 0, 0};
+  }
 };
 
 template <int CPL>
@@ -1058,6 +1072,35 @@ struct DownRows<Q4, CPL> {
 #pragma unroll
     for (int r = 0; r < 8; ++r) out[r] = q4_dequant8(c[r][q], f16x2{sc[r], sc[r]});
   }
+  // Every lane loads (stand-in rows and columns from the caller); group_ok
+  // dequantizes the rows with ok false with a zero scale.
+  __device__ __forceinline__ void load_all(const void* w, size_t scale_off, int d, const int (&rows)[8], int col) {
+    const int nbk = d / 32;
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    const f16* scales = reinterpret_cast<const f16*>(wb + scale_off);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const size_t blk = (size_t)rows[r] * nbk + col / 32;
+      const uint8_t* p = wb + blk * 16 + (col % 32) / 2;
+      if constexpr (CPL == 32) {
+        const u32x4 t = ld_nt(p);
+        c[r][0] = t.x; c[r][1] = t.y; c[r][2] = t.z; c[r][3] = t.w;
+      } else if constexpr (CPL == 16) {
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        c[r][0] = t.x; c[r][1] = t.y;
+      } else {
+        c[r][0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
+      }
+      sc[r] = scales[blk];
+    }
+  }
+  __device__ __forceinline__ void group_ok(int q, const bool (&ok)[8], u32x4 (&out)[8]) const {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const f16 s = ok[r] ? sc[r] : (f16)0.0f;
+      out[r] = q4_dequant8(c[r][q], f16x2{s, s});
+    }
+  }
 };
 
 // The GPU deals the workgroups of a launch to its 8 XCDs round-robin by
@@ -1074,7 +1117,7 @@ __device__ __forceinline__ void xcd_grouped(int& x, int& y) {
 }
 
 template <typename WF, int NB, int CPL>
-__global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w_dt, size_t scale_off, int d,
+__global__ __launch_bounds__(kMdThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_mdown(const void* __restrict__ w_dt, size_t scale_off, int d,
                                                       int d_ff, const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ count_ptr, int max_count,
                                                       const f16* __restrict__ h, int ldh, int nt, int n_chunks,
@@ -1112,40 +1155,59 @@ __global__ __launch_bounds__(kMdThreads) void k_mdown(const void* __restrict__ w
   // The list entries of step kk+1 are loaded while step kk's rows are in
   // flight (clamped to the last valid entry, so the loads carry no lane
   // condition); a step then waits for one round trip, not two.
+  // Two register stages (pipeline2): the rows and H of step kk+1 are in
+  // flight while step kk is multiplied, and the list entries of step kk+2
+  // while those are loaded.  Every lane loads (entries past the count or
+  // malformed read row 0, columns past d read column 0, H past the count
+  // reads position 0), and the unused values are zeroed when the operands
+  // are formed, so no load's issue depends on a branch.
   int nidx[8];
   auto load_idx = [&](int kk) {
     const int q0 = kk * 32 + g * 8;
 #pragma unroll
     for (int r = 0; r < 8; ++r) nidx[r] = idx[q0 + r < cnt ? q0 + r : cnt - 1];
   };
-  if (kw0 < kw1) load_idx(kw0);
-  for (int kk = kw0; kk < kw1; ++kk) {
+  const int colc = cv ? col : 0;
+  struct Stage {
+    DownRows<WF, CPL> wr;
+    bool ok[8];
+    bool hv;
+    u32x4 a[NB];
+  };
+  auto load = [&](Stage& S, int kk) {
     const int p0 = kk * 32 + g * 8;
     int rows[8];
-    bool ok[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int i = nidx[r];
-      ok[r] = cv && p0 + r < cnt && (unsigned)i < (unsigned)d_ff;
-      rows[r] = ok[r] ? i : 0;
+      S.ok[r] = cv && p0 + r < cnt && (unsigned)i < (unsigned)d_ff;
+      rows[r] = S.ok[r] ? i : 0;
     }
-    if (kk + 1 < kw1) load_idx(kk + 1);
-    DownRows<WF, CPL> wr;
-    wr.load(w_dt, scale_off, d, rows, ok, col);
+    load_idx(kk + 1 < kw1 ? kk + 1 : kk);
+    S.wr.load_all(w_dt, scale_off, d, rows, colc);
+    S.hv = p0 < cnt;
+    const int pc = S.hv ? p0 : 0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) S.a[nb] = ld16(h + (size_t)(nb * 16 + n16) * ldh + pc);
+  };
+  auto mul = [&](const Stage& S) {
     u32x4 a[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) a[nb] = p0 < cnt ? ld16(h + (size_t)(nb * 16 + n16) * ldh + p0) : u32x4{0, 0, 0, 0};
+    for (int nb = 0; nb < NB; ++nb) a[nb] = S.hv ? S.a[nb] : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int q = 0; q < CPL / 8; ++q) {
       u32x4 rw[8], bt[8];
-      wr.group(q, rw);
+      S.wr.group_ok(q, S.ok, rw);
       transpose8x8(rw, bt);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[8 * q + j][nb] = mfma(a[nb], bt[j], acc[8 * q + j][nb]);
     }
-  }
+  };
+  if (kw0 < kw1) load_idx(kw0);
+  Stage S0, S1;
+  pipeline2(kw0, kw1, S0, S1, load, mul);
 
   // ((w3 + w2) + w1) + w0 through one LDS buffer, then wave 0 writes.
   for (int w = kMdWaves - 1; w >= 1; --w) {
