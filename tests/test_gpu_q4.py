@@ -110,12 +110,15 @@ def test_sparse_ffn_q4(d, f, act, n_tok):
         check_y(host(y), ref, TOL["q4_0"], f"q4 {act} d={d} f={f} n={n_tok} density={density}")
 
 
-@pytest.mark.parametrize("d,f", [(1024, 900), (8192, 500)])
+@pytest.mark.parametrize("d,f", [(1024, 900), (8192, 500), (640, 300)])
 @pytest.mark.parametrize("act", ["relu", "reglu"])
 @pytest.mark.parametrize("n_tok", [3, 8, 9, 16, 17, 32, 33, 64, 70])
 def test_sparse_ffn_q4_mfma(d, f, act, n_tok):
     # More tokens than one list-path pass: the matrix-core path (k_mup +
     # k_mdown up to 16 tokens, the wide kernels from 17, two tiles past 64).
+    # d = 640 leaves the last column tile of the down projections part
+    # empty (256 and 512 columns per tile), so those lanes read a stand-in
+    # column and add nothing.
     ffn, hk, _ = _q4_ffn(d, f, act, seed=d + 7 * f + n_tok)
     g = torch.Generator(device="cuda").manual_seed(11 * n_tok + f)
     x = torch.randn((n_tok, d), generator=g, device="cuda").to(torch.float16)
