@@ -1572,12 +1572,14 @@ __device__ __forceinline__ void transpose8x4(const u32x2 (&in)[8], u32x4 (&out)[
 }
 
 // k_mdown_w4 (fp16 rows, 33-64 tokens): k_mdown_wide with 4 columns per lane
-// instead of 8.  Half the accumulators leave room for a second stage of rows
-// in flight (pipeline2, every lane loading: entries past the count or
-// malformed read row 0, columns past d read column 0, both zeroed when the
-// operands are formed), and with 256 columns per workgroup 16 list chunks
-// still give 512 workgroups at the Falcon width, so the partial sums that
-// the merge reads back are half as many bytes as with 32 chunks.
+// instead of 8.  Half the accumulators leave room for more rows in flight:
+// three register stages over whole pieces of kW4Piece k-steps (pipeline3x;
+// a chunk's last, partial piece takes pipeline2), every lane loading
+// (entries past the count or malformed read row 0, columns past d read
+// column 0, both zeroed when the operands are formed), held to 2 waves per
+// SIMD.  With 256 columns per workgroup 16 list chunks still give 512
+// workgroups at the Falcon width, so the partial sums that the merge reads
+// back are half as many bytes as with 32 chunks.
 constexpr int kW4Piece = 18;                 // k-steps per staged piece: a multiple of the 3 row stages
 
 template <int NB>
